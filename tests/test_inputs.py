@@ -1,0 +1,112 @@
+"""The seeded input generator: SplitMix64 stream, Box-Muller normals, fp16
+round-to-nearest-even, and the workload table."""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from scaled_dot_product_attn_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line)
+    return rows
+
+
+def test_splitmix64_published_vector():
+    want = [int(x) for x in _read_golden("splitmix64_seed1234567.txt")]
+    got = [int(x) for x in inputs.splitmix64(1234567, 5)]
+    assert got == want
+
+
+def test_splitmix64_counter_offset():
+    a = inputs.splitmix64(42, 100)
+    b = inputs.splitmix64(42, 60, start=40)
+    assert np.array_equal(a[40:], b)
+
+
+def test_uniforms_in_half_open_unit_interval():
+    u = inputs.uniform01(7, 200_000)
+    assert u.min() > 0.0 and u.max() <= 1.0
+    # mean 1/2, variance 1/12: 6-sigma sampling bounds
+    n = u.size
+    assert abs(u.mean() - 0.5) < 6 * math.sqrt(1 / 12 / n)
+
+
+def test_normals_moments():
+    x = inputs.normal_f64(11, 400_000)
+    n = x.size
+    assert abs(x.mean()) < 6 / math.sqrt(n)
+    assert abs(x.var() - 1.0) < 6 * math.sqrt(2 / n)
+    # fourth moment of N(0,1) is 3
+    assert abs((x ** 4).mean() - 3.0) < 0.1
+
+
+def test_box_muller_pairs_closed_form():
+    u = inputs.uniform01(5, 4)
+    x = inputs.normal_f64(5, 4)
+    r0 = math.sqrt(-2 * math.log(u[0]))
+    assert x[0] == pytest.approx(r0 * math.cos(2 * math.pi * u[1]), rel=1e-15)
+    assert x[1] == pytest.approx(r0 * math.sin(2 * math.pi * u[1]), rel=1e-15)
+
+
+@pytest.mark.parametrize("value,expected", [
+    (1.0 + 2.0 ** -11, 1.0),                       # tie -> even (down)
+    (1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -9),       # tie -> even (up)
+    (1.0 + 2.0 ** -11 + 2.0 ** -30, 1.0 + 2.0 ** -10),  # above tie -> up
+    (2.0 ** -25, 0.0),                             # half the least subnormal -> 0
+    (1.5 * 2.0 ** -24, 2.0 ** -23),                # subnormal tie -> even
+    (-(1.0 + 3 * 2.0 ** -11), -(1.0 + 2.0 ** -9)),  # symmetric for negatives
+    (65504.0, 65504.0),                            # largest finite
+])
+def test_fp16_round_to_nearest_even(value, expected):
+    got = np.array([value], dtype=np.float64).astype(np.float16)[0]
+    assert float(got) == expected
+
+
+def test_workloads_match_case_table():
+    rows = [r.split() for r in _read_golden("case_table.txt")]
+    assert len(rows) == 5
+    for c, row in enumerate(rows, start=1):
+        w = inputs.WORKLOADS[c]
+        B, H, S, D = map(int, row[1:5])
+        assert (w.B, w.H, w.S, w.D) == (B, H, S, D)
+        assert w.causal == (row[5] == "yes")
+    # sigma 0.5 for the head-dim-512 case, 1 elsewhere
+    assert [inputs.WORKLOADS[c].sigma for c in range(1, 6)] == [1, 1, 1, 1, 0.5]
+
+
+def test_workload_scale_is_float32_inverse_sqrt():
+    for w in inputs.WORKLOADS.values():
+        assert w.scale == float(np.float32(1 / math.sqrt(w.D)))
+
+
+def test_workload_accounting_closed_forms():
+    w = inputs.WORKLOADS[3]
+    assert w.flops() == 8_589_934_592
+    assert w.alg_bytes() == 33_685_504
+    w = inputs.WORKLOADS[1]
+    assert w.flops() == 33_554_432 and w.alg_bytes() == 528_384
+
+
+def test_generation_is_deterministic_and_seed_sensitive():
+    a = inputs.normal_f16(3000, (1, 2, 64, 128))
+    b = inputs.normal_f16(3000, (1, 2, 64, 128))
+    c = inputs.normal_f16(3001, (1, 2, 64, 128))
+    assert inputs.sha256(a) == inputs.sha256(b)
+    assert inputs.sha256(a) != inputs.sha256(c)
+    assert a.dtype == np.float16 and a.shape == (1, 2, 64, 128)
+
+
+def test_sigma_scaling_is_exact_before_rounding():
+    z = inputs.normal_f64(9, 1000)
+    x = inputs.normal_f16(9, (1000,), sigma=0.5)
+    assert np.array_equal(x, (0.5 * z).astype(np.float16))
