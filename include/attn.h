@@ -1,0 +1,112 @@
+/*
+ * attn.h - C ABI of the fused scaled-dot-product attention forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ *   O = softmax(scale * Q K^T + causal mask) V
+ *   LSE[i] = log( sum_{visible j} exp(scale * q_i . k_j) )      (natural log)
+ *
+ * The operation is the SDPA forward that "An Optimal Mapper Meets a Real GPU"
+ * lowers and gates against PyTorch SDPA (section "Ground rules": FP16 in,
+ * FP32 accumulate; section "Experiment one": query length equals key length,
+ * causal or not).  The per-row log-sum-exp output and the head-dim-512 case,
+ * whose two 256-wide halves of Q K^T are summed in logit space before the
+ * softmax, follow the STAGE_D.md notes (sections "2. External k_sub Merge is
+ * Mathematically Impossible", "4. Guard Dead Code" and "6. The k_tile
+ * Parameter").
+ *
+ * Plain C (C99), no HIP or torch types: pointers, sizes and a stream handle.
+ *
+ * Data layout (all contiguous, row-major):
+ *   q, k, v, o : fp16 (IEEE binary16 bit patterns), shape [B, H, S, D]
+ *   lse        : fp32, shape [B, H, S]
+ * All pointers are DEVICE pointers on the current HIP device.
+ *
+ * Semantics
+ *   - causal != 0 hides key j from query i when j > i (query and key lengths
+ *     are equal, so top-left and bottom-right alignment coincide).
+ *   - scale multiplies the fp32 dot product before the softmax; any finite
+ *     value is accepted (0 gives uniform weights, a negative value is applied
+ *     exactly by negating Q).
+ *   - Accumulation is fp32; P is rounded to fp16 (nearest even) before the
+ *     P V product; O is rounded to fp16 (nearest even) once, after dividing
+ *     by the row sum.
+ *   - Any S >= 1 is accepted: ragged tails are masked, never read out of
+ *     bounds.
+ *   - Deterministic: the same inputs give the same output bytes (no atomics,
+ *     fixed reduction order).
+ *
+ * Ownership and synchronisation
+ *   The caller allocates and owns every buffer; the library never allocates
+ *   or frees caller memory.  attn_fwd enqueues one kernel on `stream` and
+ *   returns without waiting; the caller synchronises.  o and lse must not
+ *   overlap the inputs or each other.
+ *
+ * Errors
+ *   Every entry point validates its arguments BEFORE any HIP call and returns
+ *   0 (ATTN_OK) or a negative ATTN_ERR_* code; nothing aborts or prints.
+ *   ATTN_ERR_LAUNCH means the kernel launch itself failed; the HIP error code
+ *   is kept per thread and returned by attn_last_hip_error().
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_OK 0
+#define ATTN_ERR_NULL -1      /* a required pointer is NULL */
+#define ATTN_ERR_SHAPE -2     /* B, H or S < 1, or the sizes overflow */
+#define ATTN_ERR_HEAD_DIM -3  /* D is not a supported head dimension */
+#define ATTN_ERR_SCALE -4     /* scale is NaN or infinite */
+#define ATTN_ERR_LAUNCH -5    /* the HIP launch failed (see attn_last_hip_error) */
+#define ATTN_ERR_WORKSPACE -6 /* workspace NULL or smaller than required */
+#define ATTN_ERR_ALIAS -7     /* an output buffer overlaps another buffer */
+
+/*
+ * Fused forward: one kernel, scores kept on chip.
+ *   q, k, v : device fp16 [B, H, S, D], read only
+ *   o       : device fp16 [B, H, S, D], written
+ *   lse     : device fp32 [B, H, S], written
+ *   D       : 64, 128 or 512 (attn_head_dim_supported tells)
+ *   stream  : a hipStream_t (NULL = the default stream)
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int S, int D, int causal, float scale, void* stream);
+
+/*
+ * Unfused three-kernel forward, kept as an ablation of the fused path: the
+ * same result computed as the three-branch pipeline QK -> softmax -> AV with
+ * its intermediates in global memory ("An Optimal Mapper Meets a Real GPU",
+ * sections "Ground rules" and "The uncomfortable audit": a multi-kernel
+ * pipeline with globally addressed workspaces).
+ *   kernel 1: S = scale * Q K^T, fp32 [B, H, S, S] (D = 512: two passes over
+ *             the head-dim halves, the second adding into S, as in option 2
+ *             of the STAGE_D.md notes);
+ *   kernel 2: P = softmax rows of S, fp16 [B, H, S, S], and LSE;
+ *   kernel 3: O = P V.
+ * workspace: device memory of at least attn_fwd_unfused_workspace_bytes(B,H,S)
+ * bytes, owned by the caller, overwritten.  Other arguments as attn_fwd.
+ */
+size_t attn_fwd_unfused_workspace_bytes(int B, int H, int S);
+int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o,
+                     float* lse, int B, int H, int S, int D, int causal,
+                     float scale, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* 1 if attn_fwd accepts head dimension D, else 0. */
+int attn_head_dim_supported(int D);
+
+/* Static text for a status code; never NULL. */
+const char* attn_status_string(int status);
+
+/* The hipError_t of this thread's last ATTN_ERR_LAUNCH (0 if none). */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,146 @@
+"""Fused scaled-dot-product attention forward for AMD Instinct MI355X.
+
+A thin ctypes binding over libattn.so (include/attn.h).  It only marshals
+arguments: every step of the computation runs in the library's HIP kernels.
+PyTorch provides device memory and the current stream.  There is no fallback:
+if the library is missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+from .build import LIB_PATH
+
+__all__ = ["AttnError", "fwd", "fwd_unfused", "unfused_workspace_bytes",
+           "head_dim_supported", "load_library", "LIB_PATH", "SYMBOLS"]
+
+# Every symbol include/attn.h declares.
+SYMBOLS = ("attn_fwd", "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
+           "attn_head_dim_supported", "attn_status_string", "attn_last_hip_error")
+
+ATTN_ERR_LAUNCH = -5
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"attn error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libattn.so (built by build.py / __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m scaled_dot_product_attn_amd.build`")
+    # Bring up torch's HIP runtime before the library registers its kernels:
+    # a library loaded ahead of torch's lazy GPU initialisation gets
+    # hipErrorNoDevice (100) from every launch.  On a machine without a GPU
+    # this only counts devices, and the library still loads for its
+    # argument-checking entry points.
+    import torch
+    if torch.cuda.is_available():
+        torch.cuda.init()
+    L = ctypes.CDLL(path)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, P]
+    L.attn_fwd.restype = I
+    L.attn_fwd_unfused.argtypes = [P, P, P, P, P, I, I, I, I, I, F, P, Z, P]
+    L.attn_fwd_unfused.restype = I
+    L.attn_fwd_unfused_workspace_bytes.argtypes = [I, I, I]
+    L.attn_fwd_unfused_workspace_bytes.restype = Z
+    L.attn_head_dim_supported.argtypes = [I]
+    L.attn_head_dim_supported.restype = I
+    L.attn_status_string.argtypes = [I]
+    L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_last_hip_error.argtypes = []
+    L.attn_last_hip_error.restype = I
+    _lib = L
+    return L
+
+
+def _check(code: int):
+    if code != 0:
+        L = load_library()
+        msg = L.attn_status_string(code).decode()
+        if code == ATTN_ERR_LAUNCH:
+            msg += f" (hipError {L.attn_last_hip_error()})"
+        raise AttnError(code, msg)
+
+
+def head_dim_supported(D: int) -> bool:
+    return bool(load_library().attn_head_dim_supported(D))
+
+
+def unfused_workspace_bytes(B: int, H: int, S: int) -> int:
+    return int(load_library().attn_fwd_unfused_workspace_bytes(B, H, S))
+
+
+def _prepare(q, k, v, out, lse, scale):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.float16:
+            raise TypeError(f"{name} must be float16, got {t.dtype}")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, S, D]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q, k, v shapes differ: {q.shape} {k.shape} {v.shape}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+    B, H, S, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.float16 or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous float16 tensor shaped like q")
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    return B, H, S, D, out, lse, float(scale), stream
+
+
+def fwd(q, k, v, *, causal: bool, scale: float | None = None, out=None, lse=None):
+    """Fused forward.  q, k, v: contiguous fp16 [B, H, S, D] on the GPU.
+    Returns (o fp16 [B, H, S, D], lse fp32 [B, H, S]).  Enqueued on the
+    current stream; asynchronous."""
+    L = load_library()
+    B, H, S, D, out, lse, scale, stream = _prepare(q, k, v, out, lse, scale)
+    _check(L.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                      lse.data_ptr(), B, H, S, D, int(bool(causal)), scale, stream))
+    return out, lse
+
+
+def fwd_unfused(q, k, v, *, causal: bool, scale: float | None = None, out=None,
+                lse=None, workspace=None):
+    """Unfused three-kernel forward (ablation).  ``workspace``: a uint8 GPU
+    tensor of at least unfused_workspace_bytes(B, H, S) bytes; allocated with
+    torch when not given."""
+    import torch
+    L = load_library()
+    B, H, S, D, out, lse, scale, stream = _prepare(q, k, v, out, lse, scale)
+    need = unfused_workspace_bytes(B, H, S)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(L.attn_fwd_unfused(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), B, H, S, D, int(bool(causal)), scale,
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                              stream))
+    return out, lse

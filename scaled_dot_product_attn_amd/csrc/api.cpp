@@ -1,0 +1,100 @@
+// C ABI of the attention forward (declared in include/attn.h).
+//
+// Every entry point validates its arguments before touching HIP, so the
+// error paths run (and are tested) on machines without a GPU.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// Shared argument checks of the fused and unfused forward.
+int validate(const void* q, const void* k, const void* v, const void* o,
+             const float* lse, int B, int H, int S, int D, float scale) {
+    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+    if (B < 1 || H < 1 || S < 1 || D < 1) return ATTN_ERR_SHAPE;
+    // Kernels index rows with 32-bit ints and launch B*H*ceil(S/32) groups at most.
+    const long long bh = (long long)B * H;
+    if (bh > INT32_MAX || (long long)S > INT32_MAX / 2 || bh * S > INT32_MAX ||
+        bh * ((S + 31) / 32) > INT32_MAX)
+        return ATTN_ERR_SHAPE;
+    if (!attn_head_dim_supported(D)) return ATTN_ERR_HEAD_DIM;
+    if (!isfinite(scale)) return ATTN_ERR_SCALE;
+    const size_t nt = (size_t)bh * S * D * 2, nl = (size_t)bh * S * 4;
+    if (overlaps(o, nt, q, nt) || overlaps(o, nt, k, nt) || overlaps(o, nt, v, nt) ||
+        overlaps(lse, nl, q, nt) || overlaps(lse, nl, k, nt) || overlaps(lse, nl, v, nt) ||
+        overlaps(lse, nl, o, nt))
+        return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+int launched(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_head_dim_supported(int D) { return D == 64 || D == 128 || D == 512; }
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int S, int D, int causal, float scale, void* stream) {
+    const int st = validate(q, k, v, o, lse, B, H, S, D, scale);
+    if (st != ATTN_OK) return st;
+    const attn::FwdArgs a{q, k, v, o, lse, B, H, S, D, causal != 0, scale, stream};
+    if (D == 512) return launched(attn::launch_fused_d512(a));
+    return launched(attn::launch_fused_d64_d128(a));
+}
+
+size_t attn_fwd_unfused_workspace_bytes(int B, int H, int S) {
+    if (B < 1 || H < 1 || S < 1) return 0;
+    // S as fp32 plus P as fp16, each [B, H, S, S]
+    return (size_t)B * H * S * S * (4 + 2);
+}
+
+int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o,
+                     float* lse, int B, int H, int S, int D, int causal,
+                     float scale, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    const int st = validate(q, k, v, o, lse, B, H, S, D, scale);
+    if (st != ATTN_OK) return st;
+    const size_t need = attn_fwd_unfused_workspace_bytes(B, H, S);
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    const size_t nt = (size_t)B * H * S * D * 2, nl = (size_t)B * H * S * 4;
+    if (overlaps(workspace, need, q, nt) || overlaps(workspace, need, k, nt) ||
+        overlaps(workspace, need, v, nt) || overlaps(workspace, need, o, nt) ||
+        overlaps(workspace, need, lse, nl))
+        return ATTN_ERR_ALIAS;
+    const attn::FwdArgs a{q, k, v, o, lse, B, H, S, D, causal != 0, scale, stream};
+    return launched(attn::launch_unfused(a, workspace));
+}
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "a required pointer is NULL";
+        case ATTN_ERR_SHAPE: return "B, H and S must be >= 1 and the sizes must fit 32-bit row indices";
+        case ATTN_ERR_HEAD_DIM: return "unsupported head dimension (supported: 64, 128, 512)";
+        case ATTN_ERR_SCALE: return "scale must be finite";
+        case ATTN_ERR_LAUNCH: return "HIP kernel launch failed (see attn_last_hip_error)";
+        case ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_fwd_unfused_workspace_bytes";
+        case ATTN_ERR_ALIAS: return "an output buffer overlaps another buffer";
+        default: return "unknown status";
+    }
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+"""The C ABI on the CPU: libattn.so loads, exports every symbol that
+include/attn.h declares, and rejects bad arguments with the documented
+status codes before any HIP call (no kernel is launched here)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import scaled_dot_product_attn_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(attn.LIB_PATH):
+        from scaled_dot_product_attn_amd import build
+        build.build()
+    return attn.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def declared_codes():
+    return {m[0]: int(m[1]) for m in
+            re.findall(r"#define\s+(ATTN_\w+)\s+(-?\d+)", open(HEADER).read())}
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert set(names) == set(attn.SYMBOLS)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for name, code in declared_codes().items():
+        s = L.attn_status_string(code).decode()
+        assert s and s != "unknown status", name
+    assert L.attn_status_string(12345).decode() == "unknown status"
+
+
+def test_head_dims(L):
+    assert [d for d in range(1, 1025) if L.attn_head_dim_supported(d)] == [64, 128, 512]
+
+
+C = declared_codes()
+# distinct fake addresses, never dereferenced: validation rejects first
+Q, K, V, O, LSE = (0x10000000 * (i + 1) for i in range(5))
+
+
+def call(L, q=Q, k=K, v=V, o=O, lse=LSE, B=1, H=2, S=64, D=64, causal=1, scale=0.125):
+    return L.attn_fwd(q, k, v, o, lse, B, H, S, D, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), "ATTN_ERR_NULL"), (dict(k=None), "ATTN_ERR_NULL"),
+    (dict(v=None), "ATTN_ERR_NULL"), (dict(o=None), "ATTN_ERR_NULL"),
+    (dict(lse=None), "ATTN_ERR_NULL"),
+    (dict(B=0), "ATTN_ERR_SHAPE"), (dict(H=-1), "ATTN_ERR_SHAPE"),
+    (dict(S=0), "ATTN_ERR_SHAPE"), (dict(D=0), "ATTN_ERR_SHAPE"),
+    (dict(B=1 << 16, H=1 << 16, S=1), "ATTN_ERR_SHAPE"),
+    (dict(B=1, H=1 << 20, S=1 << 12), "ATTN_ERR_SHAPE"),
+    (dict(D=96), "ATTN_ERR_HEAD_DIM"), (dict(D=256), "ATTN_ERR_HEAD_DIM"),
+    (dict(scale=math.nan), "ATTN_ERR_SCALE"), (dict(scale=math.inf), "ATTN_ERR_SCALE"),
+    (dict(scale=-math.inf), "ATTN_ERR_SCALE"),
+    (dict(o=Q), "ATTN_ERR_ALIAS"), (dict(lse=V + 100), "ATTN_ERR_ALIAS"),
+    (dict(lse=O), "ATTN_ERR_ALIAS"),
+])
+def test_fused_validation(L, kw, code):
+    assert call(L, **kw) == C[code]
+
+
+def test_unfused_validation(L):
+    need = L.attn_fwd_unfused_workspace_bytes(2, 3, 100)
+    assert need == 2 * 3 * 100 * 100 * 6
+    assert L.attn_fwd_unfused_workspace_bytes(0, 3, 100) == 0
+    W = 0x90000000
+    args = (Q, K, V, O, LSE, 2, 3, 100, 128, 1, 0.1)
+    assert L.attn_fwd_unfused(*args, None, need, None) == C["ATTN_ERR_WORKSPACE"]
+    assert L.attn_fwd_unfused(*args, W, need - 1, None) == C["ATTN_ERR_WORKSPACE"]
+    assert L.attn_fwd_unfused(*args, Q, need, None) == C["ATTN_ERR_ALIAS"]
+    bad = (Q, K, V, O, LSE, 2, 3, 100, 100, 1, 0.1)
+    assert L.attn_fwd_unfused(*bad, W, need, None) == C["ATTN_ERR_HEAD_DIM"]
+
+
+def test_last_hip_error_starts_clear(L):
+    assert L.attn_last_hip_error() == 0
+
+
+def test_python_binding_rejects_cpu_tensors(L):
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        attn.fwd(q, q, q, causal=True)
+    with pytest.raises(TypeError):
+        attn.fwd(q.float(), q, q, causal=True)
