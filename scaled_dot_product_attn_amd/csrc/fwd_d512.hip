@@ -1,4 +1,308 @@
+// Fused scaled-dot-product attention forward for head dimension 512 (gfx950).
+//
+// Same operation as the D = 64 / 128 kernel: O = softmax(scale Q K^T + causal
+// mask) V with fp16 in / fp32 accumulate / fp16 O and fp32 LSE, scores kept on
+// chip.  What changes at D = 512 is how Q K^T is split.  Following the notes on
+// the head-dim-512 kernel (STAGE_D.md, sections "2. External k_sub Merge is
+// Mathematically Impossible" and "6. The k_tile Parameter"), the head
+// dimension is cut into two 256-wide sub-tiles and their partial logits are
+// ADDED in logit space, S = S_0 + S_1, before any max or exp: softmax is
+// nonlinear, so merging softmax(S_0)V and softmax(S_1)V afterwards would be
+// wrong.  Here the two sub-tiles live in two different waves:
+//
+//   * A workgroup (4 waves) owns 64 query rows.  Wave w handles row group
+//     rg = w & 1 (32 rows) and head-dim half dh = w >> 1 (256 dims).
+//   * Per 32-key tile, wave (rg, dh) computes the partial S^T over its 256
+//     dims (16 v_mfma_f32_32x32x16_f16), publishes it in LDS, and adds its
+//     partner's (rg, 1-dh) partial: both waves then hold the same
+//     S = S_0 + S_1 (fp32 addition is commutative, so they agree bit for bit)
+//     and run the same online softmax.
+//   * Each wave then accumulates O^T for its own 256 output dims
+//     (16 MFMAs), reading V^T with ds_read_b64_tr_b16, like the smaller-D
+//     kernel.  Splitting P V along the output dims is what the notes call the
+//     pv_n_tile knob; it keeps a wave's output accumulator at 128 registers.
+//   * K (padded rows) and V (XOR-swizzled rows) stream through two LDS stages,
+//     staged through registers with bounds-checked buffer loads.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fwd_common.h"
 #include "kernels.h"
+
 namespace attn {
-hipError_t launch_fused_d512(const FwdArgs&) { return hipErrorNotSupported; }
+namespace {
+
+using namespace detail;
+
+struct G512 {
+    static constexpr int D = 512;
+    static constexpr int DH = 256;               // head dims per sub-tile
+    static constexpr int NW = 4;
+    static constexpr int NT = 64 * NW;
+    static constexpr int BM = 64;                // query rows per workgroup
+    static constexpr int BN = 32;                // keys per tile
+    static constexpr int NS = 2;                 // LDS stages
+    static constexpr int CPR = D / 8;            // 16-byte chunks per row
+    static constexpr int KSTR = D + 8;           // padded K row (halfs)
+    static constexpr int KTILE = BN * KSTR;
+    static constexpr int VTILE = BN * D;
+    static constexpr int STAGE = KTILE + VTILE;
+    static constexpr int XCH = NW * 16 * 64;     // floats of the S^T exchange buffer
+    static constexpr int LDS_BYTES = NS * STAGE * 2 + XCH * 4;
+    static constexpr int CH = BN * CPR / NT;     // chunks per thread per K (or V) tile
+    static_assert(CH * NT == BN * CPR, "tile split");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// V row swizzle: XOR chunk bits 2-3 with the row's low two bits, so that the
+// four rows of a transposed read hit different banks.
+__device__ __forceinline__ int swz_v512(int r) { return 4 * (r & 3); }
+
+struct Fwd512 {
+    using G = G512;
+    const _Float16* __restrict__ Q;
+    const _Float16* __restrict__ K;
+    const _Float16* __restrict__ V;
+    _Float16* __restrict__ O;
+    float* __restrict__ LSE;
+    _Float16* lds;
+    float* xch;
+    int S;
+    bool causal;
+    size_t base, lse_base;
+    float c;
+    uint32_t qsign;
+    int tid, w, lane, g, n, rg, dh;
+    u32x4 sreg[G::CH];  // staging registers: K then V of the next tile
+
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const _Float16* t, int j0) const {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<_Float16*>(t + base + (size_t)j0 * G::D), (short)0,
+            (S - j0) * G::D * 2, 0x00020000);
+    }
+    // Next-tile staging: K and V go through the same registers one after the
+    // other (K around the Q K^T phase, V around the P V phase).
+    template <bool IS_V>
+    __device__ __forceinline__ void load_part(int j) {
+        const int j0 = j * G::BN;
+        const auto r = tile_rsrc(IS_V ? V : K, j0);
+#pragma unroll
+        for (int u = 0; u < G::CH; ++u)
+            sreg[u] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (tid + G::NT * u), 0, 0));
+    }
+    template <bool IS_V>
+    __device__ __forceinline__ void store_part(int st) {
+        _Float16* Ks = lds + st * G::STAGE;
+        _Float16* Vs = Ks + G::KTILE;
+#pragma unroll
+        for (int u = 0; u < G::CH; ++u) {
+            const int ci = tid + G::NT * u;
+            const int row = ci / G::CPR, cc = ci % G::CPR;
+            if (IS_V)
+                *reinterpret_cast<u32x4*>(Vs + row * G::D + 8 * (cc ^ swz_v512(row))) = sreg[u];
+            else
+                *reinterpret_cast<u32x4*>(Ks + row * G::KSTR + 8 * cc) = sreg[u];
+        }
+    }
+
+    // Partial S^T over this wave's 256 head dims: 32 keys x 32 queries.
+    __device__ __forceinline__ floatx16 qk_half(const half8* qf, int st) const {
+        const _Float16* kp = lds + st * G::STAGE + n * G::KSTR + G::DH * dh + 8 * g;
+        floatx16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            half8 kf[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                kf[e] = *reinterpret_cast<const half8*>(kp + 16 * (4 * k4 + e));
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[e], qf[4 * k4 + e], acc, 0, 0, 0);
+        }
+        return acc;
+    }
+
+    // O^T (this wave's 256 dims) += V^T P^T for the 32-key tile in stage st.
+    __device__ __forceinline__ void pv_half(floatx16* o, const half8* pf, int st) const {
+        const _Float16* Vs = lds + st * G::STAGE + G::KTILE;
+        const int n16 = n >> 4, jj = n & 15;
+        const int sub = (jj & 3) >> 1, half = jj & 1;
+        const int sw = swz_v512(jj >> 2);  // (row & 3) == jj >> 2 for every row read
+        const _Float16* rowp = Vs + (4 * g + (jj >> 2)) * G::D + 4 * half;
+#pragma unroll
+        for (int b = 0; b < G::DH / 32; ++b) {
+            const _Float16* pb = rowp + 8 * ((32 * dh + 4 * b + 2 * n16 + sub) ^ sw);
+            half8 a[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                half4 part[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    part[t] = __builtin_bit_cast(
+                        half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                                   (lds_half4*)(pb + (16 * h + 8 * t) * G::D)));
+                a[h] = half8{part[0][0], part[0][1], part[0][2], part[0][3],
+                             part[1][0], part[1][1], part[1][2], part[1][3]};
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[h], pf[h], o[b], 0, 0, 0);
+        }
+    }
+
+    __device__ void run(int qt) {
+        const int q0 = qt * G::BM;
+        const int row = q0 + 32 * rg + n;
+        const int r_lo = q0 + 32 * rg, r_hi = r_lo + 31;
+        const int kv_end = causal ? min(S, q0 + G::BM) : S;
+        const int nT = (kv_end + G::BN - 1) / G::BN;
+
+        // Q^T fragment of this wave's rows and head-dim half.
+        half8 qf[G::DH / 16];
+        {
+            const u32x4* src = reinterpret_cast<const u32x4*>(
+                Q + base + (size_t)min(row, S - 1) * G::D + G::DH * dh);
+#pragma unroll
+            for (int kk = 0; kk < G::DH / 16; ++kk) {
+                u32x4 x = src[2 * kk + g];
+                x ^= qsign;
+                qf[kk] = __builtin_bit_cast(half8, x);
+            }
+        }
+
+        float m = kNegInf, l = 0.f;
+        floatx16 o[G::DH / 32];
+#pragma unroll
+        for (int b = 0; b < G::DH / 32; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
+
+        load_part<false>(0);
+        store_part<false>(0);
+        load_part<true>(0);
+        store_part<true>(0);
+        barrier();
+        float* mine = xch + w * 16 * 64;
+        const float* other = xch + (w ^ 2) * 16 * 64;  // same row group, other half
+        for (int i = 0; i < nT; ++i) {
+            const int j0 = i * G::BN;
+            const int jn = min(i + 1, nT - 1);  // past the end: reload the last tile
+            load_part<false>(jn);
+            const bool skip = causal && j0 > r_hi;  // every key is in this wave's future
+            floatx16 s;
+            if (!skip) {
+                s = qk_half(qf, i & 1);
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    *reinterpret_cast<float4*>(mine + (4 * q4) * 64 + 4 * lane) =
+                        float4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
+            }
+            store_part<false>((i + 1) & 1);  // stage of tile i-1, free since the last barrier
+            load_part<true>(jn);
+            barrier();  // both sub-tile partials are published
+            if (!skip) {
+                // S = S_0 + S_1 in logit space (the same sum in both waves)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const float4 p = *reinterpret_cast<const float4*>(other + (4 * q4) * 64 + 4 * lane);
+                    s[4 * q4] += p.x;
+                    s[4 * q4 + 1] += p.y;
+                    s[4 * q4 + 2] += p.z;
+                    s[4 * q4 + 3] += p.w;
+                }
+                half8 pf[2];
+                const int lim = (causal ? min(row, S - 1) : S - 1) - (j0 + 4 * g);
+                const bool need_mask = (causal && j0 + G::BN - 1 > r_lo) || (j0 + G::BN > S);
+                if (need_mask)
+                    online_softmax<true, G::DH / 32>(s, lim, c, m, l, o, pf);
+                else
+                    online_softmax<false, G::DH / 32>(s, lim, c, m, l, o, pf);
+                pv_half(o, pf, i & 1);
+            }
+            store_part<true>((i + 1) & 1);
+            barrier();  // next tile in LDS; exchange buffer free again
+        }
+
+        // Epilogue: both waves of a row group hold the same m and l; each
+        // writes its 256 output dims.
+        const float lt = sum_halves(l);
+        const float inv = 1.0f / lt;
+        if (row < S) {
+            _Float16* orow = O + base + (size_t)row * G::D + G::DH * dh;
+#pragma unroll
+            for (int b = 0; b < G::DH / 32; ++b)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    u32x2 pk;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const _Float16 lo = (_Float16)(o[b][4 * q4 + 2 * h] * inv);
+                        const _Float16 hi = (_Float16)(o[b][4 * q4 + 2 * h + 1] * inv);
+                        pk[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+                    }
+                    *reinterpret_cast<u32x2*>(orow + 32 * b + 8 * q4 + 4 * g) = pk;
+                }
+            if (dh == 0 && g == 0) LSE[lse_base + row] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
+        }
+    }
+};
+
+__global__ void __launch_bounds__(256, 1)
+fwd512_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
+              const _Float16* __restrict__ V, _Float16* __restrict__ O,
+              float* __restrict__ LSE, int BH, int S, int causal, float c, uint32_t qsign)
+{
+    using G = G512;
+    __shared__ __attribute__((aligned(1024))) _Float16 lds[G::NS * G::STAGE + 2 * G::XCH];
+
+    const int T = (S + G::BM - 1) / G::BM;
+    const int bh = blockIdx.x % BH;
+    int qt = blockIdx.x / BH;
+    if (causal) qt = T - 1 - qt;  // longest rows first
+
+    Fwd512 f;
+    f.Q = Q;
+    f.K = K;
+    f.V = V;
+    f.O = O;
+    f.LSE = LSE;
+    f.lds = lds;
+    f.xch = reinterpret_cast<float*>(lds + G::NS * G::STAGE);
+    f.S = S;
+    f.causal = causal != 0;
+    f.base = (size_t)bh * S * G::D;
+    f.lse_base = (size_t)bh * S;
+    f.c = c;
+    f.qsign = qsign;
+    f.tid = threadIdx.x;
+    f.w = threadIdx.x >> 6;
+    f.lane = threadIdx.x & 63;
+    f.g = f.lane >> 5;
+    f.n = f.lane & 31;
+    f.rg = f.w & 1;
+    f.dh = f.w >> 1;
+    f.run(qt);
 }
+
+hipError_t launch(const FwdArgs& a) {
+    using G = G512;
+    const int T = (a.S + G::BM - 1) / G::BM;
+    const long long blocks = (long long)a.B * a.H * T;
+    const float c = fabsf(a.scale) * 1.44269504088896340736f;
+    const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
+    hipLaunchKernelGGL(fwd512_kernel, dim3((unsigned)blocks), dim3(G::NT), 0,
+                       (hipStream_t)a.stream,
+                       (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,
+                       (_Float16*)a.o, a.lse, a.B * a.H, a.S, a.causal, c, qsign);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fused_d512(const FwdArgs& a) { return launch(a); }
+
+}  // namespace attn

@@ -10,23 +10,46 @@
 // row maximum (the "O rescale (kt>0)" step of the STAGE_D.md notes).
 //
 // Work decomposition
-//   * one workgroup = 4 waves = 128 query rows of one (batch, head); each wave
-//     owns 32 consecutive rows for the whole key loop.
-//   * keys stream in tiles of 64 through double-buffered LDS: K row-major,
-//     V transposed.  Global loads for tile j+1 are in flight while tile j is
-//     computed.  Under causal masking tiles past the diagonal are never loaded
-//     and 32-key blocks a wave cannot see are skipped.
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_f16 (A = 32 keys x 16 dims from LDS,
-//     B = Q^T fragment held in VGPRs for the whole loop).  In the 32x32
-//     accumulator a lane holds one query column and 16 keys, so the row max
-//     needs one exchange between the two 32-lane halves and the per-row
-//     statistics m, l live in the lane that owns the query.
+//   * A workgroup (4 waves) owns 64-row query tiles of one (batch, head).
+//     Under causal masking it processes a pair of tiles, t and T-1-t, so that
+//     every workgroup does the same number of key tiles (T+1): the causal
+//     triangle is balanced across the chip instead of leaving the
+//     last-row workgroups as a long tail.
+//   * Keys stream through LDS in 64-key tiles.  Each tile is fetched with
+//     bounds-checked buffer loads (rows past S read as zero) into one of two
+//     register sets two steps ahead of its use, then written to one of four
+//     LDS stages; tiles past the causal diagonal are never loaded.  (The
+//     loads go through registers rather than straight into LDS because the
+//     compiler drains every outstanding LDS-direct load before a transposed
+//     LDS read.)
+//   * Wave w handles query rows 32*(w&1) .. +31 of the tile against keys
+//     32*(w>>1) .. +31 of every key tile (two row groups x two key halves), so
+//     all four SIMDs work on every tile.  Each wave keeps its own running
+//     max / sum / output over its key half; the two halves are merged at the
+//     end in a fixed order (deterministic).  This is the online-softmax merge
+//     over DISJOINT key sets, which is exact, unlike merging head-dim partial
+//     products after the softmax.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_f16: A = 32 keys x 16 dims read from
+//     LDS, B = the wave's Q^T fragment kept in VGPRs for the whole tile.  In
+//     the 32x32 accumulator each lane holds one query and 16 keys, so row
+//     statistics live in the lane that owns the query and the row max needs one
+//     exchange between the two 32-lane halves.
 //   * O^T += V^T P^T on the same MFMA: P^T (fp16, round-to-nearest-even) is the
-//     B operand straight from the softmax registers, and V^T comes from LDS in
-//     a key order that matches the accumulator layout (keys 4..7 and 8..11 of
-//     each 16-key group swapped), so no lane shuffles are needed.
-//   * exp2 on v_exp_f32 with scale*log2(e) folded into one FMA; the O^T
-//     rescale is per lane.
+//     B operand straight from the softmax registers; V^T is read from the
+//     row-major V tile with ds_read_b64_tr_b16, which hands each lane four
+//     consecutive keys of one head-dim column.  The accumulator's key order
+//     (8(r/4) + 4g + r%4) is exactly the order two transposed reads deliver.
+//   * Software pipelining: the Q K^T of tile i is issued next to the
+//     softmax of tile i-1, so MFMA and VALU work of one wave overlap; all LDS
+//     reads of a step are issued before its MFMAs.
+//   * exp2 on v_exp_f32 with scale*log2(e) folded into one FMA.  The output
+//     is rescaled lazily: the reference max only moves when a row max grows
+//     by more than 2^8, which keeps every weight <= 256 and skips most
+//     rescales (the result is the same up to rounding).
+//
+// LDS layouts are XOR-swizzled in 16-byte chunks (no padding) so that the
+// 16 lanes of a ds_read_b128 (K) and the 32 lanes of a transposed read (V)
+// hit distinct banks.
 //
 // MFMA lane layouts used (32x32x16, wave64, g = lane / 32, n = lane % 32):
 //   A[m][k]: lane holds m = n, k = 8g .. 8g+7
@@ -35,265 +58,384 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fwd_common.h"
 #include "kernels.h"
 
 namespace attn {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kNegInf = -__builtin_inff();
-constexpr float kLn2 = 0.693147180559945309417f;
+using namespace detail;
 
 template <int D>
-struct Cfg {
-    static constexpr int NW = 4;             // waves per workgroup
-    static constexpr int NT = NW * 64;       // threads per workgroup
-    static constexpr int BM = 32 * NW;       // query rows per workgroup
-    static constexpr int BN = 64;            // keys per tile
-    static constexpr int KSTR = D + 8;       // K row stride in LDS (halfs); +16 B
-    static constexpr int VSTR = BN + 8;      // V^T row stride in LDS (halfs)
-    static constexpr int K_HALFS = BN * KSTR;
-    static constexpr int V_HALFS = D * VSTR;
-    static constexpr int STAGE = K_HALFS + V_HALFS;
-    static constexpr int LDS_BYTES = 2 * STAGE * 2;
-    static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-    static constexpr int KCH = BN * CPR / NT;         // K chunks per thread
-    static constexpr int VR = BN * D / 8 / NT;        // keys per thread (V^T)
-    static constexpr int VKG = BN / VR;               // key groups per d-block
-    static_assert(KCH * NT == BN * CPR, "K tile must split evenly");
-    static_assert(VR == 2 || VR == 4, "V transpose handles 2 or 4 keys");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+struct Geo {
+    static constexpr int NW = 4;                 // waves per workgroup
+    static constexpr int NT = 64 * NW;           // threads
+    static constexpr int BM = 64;                // query rows per tile
+    static constexpr int BN = 64;                // keys per tile
+    static constexpr int NS = 4;                 // LDS stages
+    static constexpr int CPR = D / 8;            // 16-byte chunks per row
+    static constexpr int KSTR = D + 8;           // K row stride in halfs (16 B pad)
+    static constexpr int KTILE = BN * KSTR;      // halfs in a K tile
+    static constexpr int VTILE = BN * D;         // halfs in a V tile (swizzled, no pad)
+    static constexpr int STAGE = KTILE + VTILE;
+    static constexpr int LDS_HALFS = NS * STAGE;
+    static constexpr int CH = BN * CPR / NT;     // 16-byte chunks per thread per K (or V) tile
+    static_assert(D == 64 || D == 128, "D");
+    static_assert(CH * NT == BN * CPR, "tile split");
+    static_assert(LDS_HALFS * 2 <= 160 * 1024, "LDS budget");
+    static_assert((D * 64 + 256) * 4 <= LDS_HALFS * 2, "merge buffer fits");
 };
 
-// Position of key x (0..63) inside a V^T row: bits 2 and 3 swapped, so that
-// the 8 keys a lane half feeds to one PV MFMA step are contiguous.
-__device__ __forceinline__ int vt_pos(int x) {
-    return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
-}
-
-__device__ __forceinline__ float xor32(float x) {
-    return __shfl_xor(x, 32, 64);
+// Swizzles (chunk index XOR), see the header comment.
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+    return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2)
-fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
-           const _Float16* __restrict__ V, _Float16* __restrict__ O,
-           float* __restrict__ LSE, int BH, int S, float c_scale, uint32_t qsign)
-{
-    using C = Cfg<D>;
-    __shared__ __attribute__((aligned(16))) _Float16 lds[2 * C::STAGE];
+struct Fwd {
+    using G = Geo<D>;
 
-    const int T = (S + C::BM - 1) / C::BM;
-    const int bh = blockIdx.x % BH;
-    int qt = blockIdx.x / BH;
-    if (CAUSAL) qt = T - 1 - qt;  // longest rows first
-    const int q0 = qt * C::BM;
-    const size_t base = (size_t)bh * S * D;
+    const _Float16* __restrict__ Q;
+    const _Float16* __restrict__ K;
+    const _Float16* __restrict__ V;
+    _Float16* __restrict__ O;
+    float* __restrict__ LSE;
+    _Float16* lds;
+    int S;
+    size_t base;      // element offset of this (batch, head)
+    size_t lse_base;  // LSE offset of this (batch, head)
+    float c;          // |scale| * log2(e)
+    uint32_t qsign;   // 0x80008000 when the scale is negative (Q negated)
+    int tid, lane, g, n, rg, kh;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const int g = lane >> 5, n = lane & 31;
-    const int row = q0 + 32 * w + n;        // the query this lane owns
-    const int r_lo = q0 + 32 * w, r_hi = r_lo + 31;
+    // Two register sets stage K/V tiles between global memory and LDS.
+    u32x4 kreg[2][G::CH];
+    u32x4 vreg[2][G::CH];
 
-    // Q^T fragments for the whole key loop: lane holds Q[row][16kk + 8g .. +7].
-    half8 qf[D / 16];
-    {
-        const bool ok = row < S;
-        const u32x4* src = reinterpret_cast<const u32x4*>(Q + base + (size_t)(ok ? row : 0) * D);
+    // Per-tile buffer resources: base = first key row of the tile, size = the
+    // rows left in this (batch, head), so rows past S read as zero.
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const _Float16* t, int j0) const {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<_Float16*>(t + base + (size_t)j0 * D), (short)0,
+            (S - j0) * D * 2, 0x00020000);
+    }
+    // Pull this workgroup's share (rows [r0, r1)) of the head's K and V into
+    // the L2: one dword per 128-byte line.  All workgroups of a head stream the
+    // same key tiles in near lockstep, so without this every tile load of every
+    // workgroup waits for a full memory round trip; with it they hit in L2.
+    // Returns a value derived from the loads so that they are kept.
+    __device__ __forceinline__ uint32_t warm_l2(int r0, int r1) const {
+        if (r1 <= r0) return 0;
+        const int nbytes = (r1 - r0) * D * 2;
+        const auto rk = tile_rsrc(K, r0), rv = tile_rsrc(V, r0);
+        uint32_t acc = 0;
+        for (int off = 128 * tid; off < nbytes; off += 128 * G::NT)
+            acc ^= __builtin_amdgcn_raw_buffer_load_b32(rk, off, 0, 0) ^
+                   __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0);
+        return acc;
+    }
+
+    template <int P>
+    __device__ __forceinline__ void load_tile(int j) {
+        const int j0 = j * G::BN;
+        const auto rk = tile_rsrc(K, j0), rv = tile_rsrc(V, j0);
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            u32x4 x = ok ? src[2 * kk + g] : u32x4{0, 0, 0, 0};
-            x ^= qsign;  // exact negation when the scale is negative
-            qf[kk] = __builtin_bit_cast(half8, x);
+        for (int u = 0; u < G::CH; ++u) {
+            const int ci = tid + G::NT * u;  // byte offset of chunk ci is 16 * ci
+            kreg[P][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * ci, 0, 0));
+            vreg[P][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 16 * ci, 0, 0));
+        }
+    }
+    template <int P>
+    __device__ __forceinline__ void store_tile(int st) {
+        _Float16* Ks = lds + st * G::STAGE;
+        _Float16* Vs = Ks + G::KTILE;
+#pragma unroll
+        for (int u = 0; u < G::CH; ++u) {
+            const int ci = tid + G::NT * u;
+            const int row = ci / G::CPR, cc = ci % G::CPR;
+            *reinterpret_cast<u32x4*>(Ks + row * G::KSTR + 8 * cc) = kreg[P][u];
+            *reinterpret_cast<u32x4*>(Vs + row * D + 8 * (cc ^ swz_v<D>(row))) = vreg[P][u];
         }
     }
 
-    const int kv_end = CAUSAL ? min(S, q0 + C::BM) : S;
-    const int nT = (kv_end + C::BN - 1) / C::BN;
+    // K fragments of this wave's 32 keys (A operand of S^T = K Q^T).
+    __device__ __forceinline__ void read_k(half8* kf, int st) const {
+        const _Float16* kp = lds + st * G::STAGE + (32 * kh + n) * G::KSTR + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) kf[kk] = *reinterpret_cast<const half8*>(kp + 16 * kk);
+    }
+    __device__ __forceinline__ floatx16 qk(const half8* kf, const half8* qf) const {
+        floatx16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kk], qf[kk], acc, 0, 0, 0);
+        return acc;
+    }
 
-    // Staging registers for the next tile.
-    u32x4 kreg[C::KCH];
-    u32x4 vreg[C::VR];
-    const int vkb = tid % C::VKG, vdb = tid / C::VKG;
-
-    auto gload = [&](int j0) {
+    // V^T fragments (A operand of O^T += V^T P^T) via transposed LDS reads:
+    // vf[h][b] covers keys 32kh + 16h .. +15 and head dims 32b .. +31.
+    __device__ __forceinline__ void read_v(half8 (*vf)[D / 32], int st) const {
+        const _Float16* Vs = lds + st * G::STAGE + G::KTILE;
+        const int n16 = n >> 4, jj = n & 15;
+        const int sub = (jj & 3) >> 1, half = (jj & 1);
+        // row & 3 == jj >> 2 for every (h, t): the swizzle is fixed per lane
+        const int sw = swz_v<D>(jj >> 2);
+        const _Float16* rowp = Vs + (32 * kh + 4 * g + (jj >> 2)) * D + 4 * half;
 #pragma unroll
-        for (int u = 0; u < C::KCH; ++u) {
-            const int ci = tid + C::NT * u;
-            const int r = ci / C::CPR, c8 = ci % C::CPR;
-            const int key = j0 + r;
-            kreg[u] = key < S ? *reinterpret_cast<const u32x4*>(K + base + (size_t)key * D + 8 * c8)
-                              : u32x4{0, 0, 0, 0};
-        }
+        for (int b = 0; b < D / 32; ++b) {
+            const _Float16* pb = rowp + 8 * ((4 * b + 2 * n16 + sub) ^ sw);
 #pragma unroll
-        for (int v = 0; v < C::VR; ++v) {
-            const int key = j0 + vkb * C::VR + v;
-            vreg[v] = key < S ? *reinterpret_cast<const u32x4*>(V + base + (size_t)key * D + 8 * vdb)
-                              : u32x4{0, 0, 0, 0};
-        }
-    };
-
-    auto lstore = [&](int buf) {
-        _Float16* Ks = lds + buf * C::STAGE;
-        _Float16* Vt = Ks + C::K_HALFS;
+            for (int h = 0; h < 2; ++h) {
+                half4 part[2];
 #pragma unroll
-        for (int u = 0; u < C::KCH; ++u) {
-            const int ci = tid + C::NT * u;
-            const int r = ci / C::CPR, c8 = ci % C::CPR;
-            *reinterpret_cast<u32x4*>(Ks + r * C::KSTR + 8 * c8) = kreg[u];
-        }
-        // Transpose VR keys x 8 dims into 8 rows of V^T.
-        const int pos = vt_pos(vkb * C::VR);
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-            const int wi = dd >> 1;
-            const bool hi = dd & 1;
-            uint32_t pk[C::VR / 2];
-#pragma unroll
-            for (int v = 0; v < C::VR / 2; ++v) {
-                const uint32_t a = vreg[2 * v][wi], b = vreg[2 * v + 1][wi];
-                pk[v] = hi ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+                for (int t = 0; t < 2; ++t)
+                    part[t] = __builtin_bit_cast(
+                        half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                                   (lds_half4*)(pb + (16 * h + 8 * t) * D)));
+                vf[h][b] = half8{part[0][0], part[0][1], part[0][2], part[0][3],
+                                 part[1][0], part[1][1], part[1][2], part[1][3]};
             }
-            _Float16* dst = Vt + (8 * vdb + dd) * C::VSTR + pos;
-            if constexpr (C::VR == 4)
-                *reinterpret_cast<u32x2*>(dst) = u32x2{pk[0], pk[1]};
-            else
-                *reinterpret_cast<uint32_t*>(dst) = pk[0];
         }
-    };
-
-    float m = kNegInf;  // running max of the scaled logits, log2 units
-    float l = 0.f;      // this lane's share of the running row sum
-    floatx16 o[D / 32];
+    }
+    __device__ __forceinline__ void pv(floatx16* o, const half8 (*vf)[D / 32],
+                                       const half8* pf) const {
 #pragma unroll
-    for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
-    for (int j = 0; j < nT; ++j) {
-        const int j0 = j * C::BN;
-        if (j + 1 < nT) gload(j0 + C::BN);
-        const _Float16* Ks = lds + (j & 1) * C::STAGE;
-        const _Float16* Vt = Ks + C::K_HALFS;
-
-        const bool wave_skip = CAUSAL && j0 > r_hi;  // every key is in this wave's future
-        if (!wave_skip) {
-            const bool need_mask = (CAUSAL && j0 + C::BN - 1 > r_lo) || (j0 + C::BN > S);
-            bool blk_on[2];
-            floatx16 s[2];
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                blk_on[c] = !(CAUSAL && j0 + 32 * c > r_hi);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[c][r] = 0.f;
-                if (blk_on[c]) {
-                    const _Float16* kp = Ks + (32 * c + n) * C::KSTR + 8 * g;
-#pragma unroll
-                    for (int kk = 0; kk < D / 16; ++kk) {
-                        const half8 a = *reinterpret_cast<const half8*>(kp + 16 * kk);
-                        s[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[kk], s[c], 0, 0, 0);
-                    }
-                }
-            }
-
-            // visibility of each accumulator entry (only on boundary tiles)
-            auto visible = [&](int c, int r) {
-                const int key = j0 + 32 * c + 8 * (r >> 2) + 4 * g + (r & 3);
-                return blk_on[c] && key < S && (!CAUSAL || key <= row);
-            };
-
-            float mx = kNegInf;
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float x = (need_mask && !visible(c, r)) ? kNegInf : s[c][r];
-                    mx = fmaxf(mx, x);
-                }
-            mx = fmaxf(mx, xor32(mx));
-            // A row with no visible key in this tile keeps its old max; clamping
-            // keeps c_scale * mx finite for c_scale = 0.
-            const float m_new = fmaxf(m, c_scale * fmaxf(mx, -3.402823466e38f));
-            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-            m = m_new;
-
-            float psum = 0.f;
-            half8 pf[4];
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][r], c_scale, -m_new));
-                    if (need_mask && !visible(c, r)) p = 0.f;
-                    psum += p;
-                    pf[2 * c + (r >> 3)][r & 7] = (_Float16)p;
-                }
-            l = l * alpha + psum;
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
+                o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[h][b], pf[h], o[b], 0, 0, 0);
+    }
 
+    // Online softmax of this wave's S^T block (keys j0 + 32kh + ...).
+    template <bool MASK>
+    __device__ __forceinline__ void softmax(const floatx16& s, int j0, int row, float& m, float& l,
+                                            floatx16* o, half8* pf) const {
+        // visibility: key <= min(row, S-1) (causal) or key <= S-1
+        const int lim = (CAUSAL ? min(row, S - 1) : S - 1) - (j0 + 32 * kh + 4 * g);
+        online_softmax<MASK, D / 32>(s, lim, c, m, l, o, pf);
+    }
+
+    // One pipeline step i >= 1 (P = i % 2, ST = i % NS): tile i+2 -> registers,
+    // S_i = Q K_i^T next to the softmax of tile i-1, P_{i-1} V_{i-1}, tile i+1
+    // -> LDS.
+    template <int P, int ST>
+    __device__ __forceinline__ void step(int i, int nT, const half8* qf, floatx16& s_cur,
+                                         int row, float& m, float& l, floatx16* o) {
+        barrier();  // tile i is in LDS; every wave is past step i-1
+        // Unconditional (past the end it re-reads the last tile, which is
+        // cache-resident) so that the compiler's wait before the LDS stores of
+        // tile i+1 counts these loads as younger and leaves them in flight.
+        load_tile<P>(min(i + 2, nT - 1));
+        // all LDS reads of the step first: one LDS latency, then back-to-back MFMAs
+        half8 kf[D / 16];
+        half8 vf[2][D / 32];
+        read_k(kf, ST);
+        read_v(vf, (ST + G::NS - 1) % G::NS);
+        const floatx16 s_next = qk(kf, qf);
+        half8 pf[2];
+        softmax<false>(s_cur, (i - 1) * G::BN, row, m, l, o, pf);
+        pv(o, vf, pf);
+        store_tile<1 - P>((ST + 1) % G::NS);  // past the end: a free stage, never read
+        s_cur = s_next;
+    }
+
+    __device__ void run_tile_rows(int qt) {
+        const int q0 = qt * G::BM;
+        const int row = q0 + 32 * rg + n;  // the query this lane owns
+        const int T = (S + G::BN - 1) / G::BN;
+        const int nT = CAUSAL ? qt + 1 : T;
+        const bool mask_last = CAUSAL || (S % G::BN) != 0;
+
+        // Q^T fragment: lane holds Q[row][16kk + 8g .. +7] (rows past S read row S-1).
+        half8 qf[D / 16];
+        {
+            const u32x4* src = reinterpret_cast<const u32x4*>(Q + base + (size_t)min(row, S - 1) * D);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                if (!blk_on[ks >> 1]) continue;
-                const _Float16* vp = Vt + n * C::VSTR + 16 * ks + 8 * g;
-#pragma unroll
-                for (int b = 0; b < D / 32; ++b) {
-                    const half8 a = *reinterpret_cast<const half8*>(vp + 32 * b * C::VSTR);
-                    o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], o[b], 0, 0, 0);
-                }
+            for (int kk = 0; kk < D / 16; ++kk) {
+                u32x4 x = src[2 * kk + g];
+                x ^= qsign;
+                qf[kk] = __builtin_bit_cast(half8, x);
             }
         }
 
-        if (j + 1 < nT) lstore((j + 1) & 1);
-        __syncthreads();
-    }
+        // prologue: tiles 0 and 1 to registers, tile 0 to LDS, tile 2 to
+        // registers, S_0, tile 1 to LDS
+        load_tile<0>(0);
+        load_tile<1>(min(1, nT - 1));
+        store_tile<0>(0);
+        barrier();
+        load_tile<0>(min(2, nT - 1));
+        floatx16 s_cur;
+        {
+            half8 kf[D / 16];
+            read_k(kf, 0);
+            s_cur = qk(kf, qf);
+        }
+        store_tile<1>(1);
 
-    // Epilogue: O = O^T / l in fp16 (round to nearest even), LSE in natural log.
-    const float lt = l + xor32(l);
-    const float inv = 1.0f / lt;
-    if (row < S) {
-        _Float16* orow = O + base + (size_t)row * D;
+        float m = kNegInf, l = 0.f;
+        floatx16 o[D / 32];
 #pragma unroll
         for (int b = 0; b < D / 32; ++b)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                u32x2 pk;
+            for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
+
+        static_assert(G::NS == 4, "the step loop is unrolled by the stage count");
+        int i = 1;
+        for (; i + 3 < nT; i += 4) {
+            step<1, 1>(i, nT, qf, s_cur, row, m, l, o);
+            step<0, 2>(i + 1, nT, qf, s_cur, row, m, l, o);
+            step<1, 3>(i + 2, nT, qf, s_cur, row, m, l, o);
+            step<0, 0>(i + 3, nT, qf, s_cur, row, m, l, o);
+        }
+        if (i < nT) step<1, 1>(i, nT, qf, s_cur, row, m, l, o);
+        if (i + 1 < nT) step<0, 2>(i + 1, nT, qf, s_cur, row, m, l, o);
+        if (i + 2 < nT) step<1, 3>(i + 2, nT, qf, s_cur, row, m, l, o);
+
+        // last tile: the only one that can need a mask
+        {
+            half8 pf[2];
+            const int jl = (nT - 1) * G::BN;
+            half8 vf[2][D / 32];
+            read_v(vf, (nT - 1) % G::NS);
+            if (mask_last)
+                softmax<true>(s_cur, jl, row, m, l, o, pf);
+            else
+                softmax<false>(s_cur, jl, row, m, l, o, pf);
+            pv(o, vf, pf);
+        }
+
+        // Merge the two key halves: kh = 1 waves publish (m, l, O^T) in LDS,
+        // kh = 0 waves combine them with their own and write the result.
+        barrier();  // every wave is done reading the stages
+        // merge buffer: float4 slots [rg][b][q4][lane] of O^T, then m, l [rg][lane]
+        float4* mo = reinterpret_cast<float4*>(lds) + rg * (D / 8) * 64;
+        float* mm = reinterpret_cast<float*>(lds) + 2 * (D / 2) * 64 + rg * 128;
+        if (kh == 1) {
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const _Float16 lo = (_Float16)(o[b][4 * q4 + 2 * h] * inv);
-                    const _Float16 hi = (_Float16)(o[b][4 * q4 + 2 * h + 1] * inv);
-                    pk[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+            for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    mo[(4 * b + q4) * 64 + lane] =
+                        float4{o[b][4 * q4], o[b][4 * q4 + 1], o[b][4 * q4 + 2], o[b][4 * q4 + 3]};
+            mm[lane] = m;
+            mm[64 + lane] = l;
+        }
+        barrier();
+        if (kh == 0) {
+            const float m1 = mm[lane], l1 = mm[64 + lane];
+            const float mt = fmaxf(m, m1);
+            const float a0 = __builtin_amdgcn_exp2f(m - mt), a1 = __builtin_amdgcn_exp2f(m1 - mt);
+            const float lt = sum_halves(l * a0 + l1 * a1);
+            const float inv = 1.0f / lt;
+            const float f0 = a0 * inv, f1 = a1 * inv;
+            // x[b][q4] packs head dims 32b + 8q4 + 4g .. +3 as two fp16 pairs
+            u32x2 x[D / 32][4];
+#pragma unroll
+            for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const float4 p1 = mo[(4 * b + q4) * 64 + lane];
+                    const float y0 = o[b][4 * q4] * f0 + p1.x * f1;
+                    const float y1 = o[b][4 * q4 + 1] * f0 + p1.y * f1;
+                    const float y2 = o[b][4 * q4 + 2] * f0 + p1.z * f1;
+                    const float y3 = o[b][4 * q4 + 3] * f0 + p1.w * f1;
+                    x[b][q4][0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y0) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y1) << 16);
+                    x[b][q4][1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y2) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y3) << 16);
                 }
-                *reinterpret_cast<u32x2*>(orow + 32 * b + 8 * q4 + 4 * g) = pk;
+            if (row < S) {
+                // Swap halves between lanes n and n+32 so that each lane holds 8
+                // consecutive head dims: lane (g=0) keeps q4 = 0, 2 and receives
+                // the partner's, lane (g=1) keeps q4 = 1, 3.
+                _Float16* orow = O + base + (size_t)row * D;
+#pragma unroll
+                for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+                    for (int qq = 0; qq < 2; ++qq) {
+                        // g=0 sends its q4 = 2qq+1 part, g=1 its q4 = 2qq part
+                        u32x2 send = g ? x[b][2 * qq] : x[b][2 * qq + 1];
+                        u32x2 keep = g ? x[b][2 * qq + 1] : x[b][2 * qq];
+                        u32x2 got;
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) got[e] = (uint32_t)__shfl_xor((int)send[e], 32, 64);
+                        // g=0: dims 32b+16qq + 0..3 (keep), 4..7 (got); g=1: dims +8..11 (got), 12..15 (keep)
+                        const u32x4 v = g ? u32x4{got[0], got[1], keep[0], keep[1]}
+                                          : u32x4{keep[0], keep[1], got[0], got[1]};
+                        *reinterpret_cast<u32x4*>(orow + 32 * b + 16 * qq + 8 * g) = v;
+                    }
+                if (g == 0) LSE[lse_base + row] = (mt + __builtin_amdgcn_logf(lt)) * kLn2;
             }
-        if (g == 0) LSE[(size_t)bh * S + row] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
+        }
+        barrier();  // the merge buffer is free again before the next tile's stores
     }
+};
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1)
+fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
+           const _Float16* __restrict__ V, _Float16* __restrict__ O,
+           float* __restrict__ LSE, int BH, int S, float c, uint32_t qsign)
+{
+    using G = Geo<D>;
+    __shared__ __attribute__((aligned(1024))) _Float16 lds[G::LDS_HALFS];
+
+    const int bh = blockIdx.x % BH;
+    const int p = blockIdx.x / BH;
+    const int T = (S + G::BM - 1) / G::BM;
+
+    Fwd<D, CAUSAL> f;
+    f.Q = Q;
+    f.K = K;
+    f.V = V;
+    f.O = O;
+    f.LSE = LSE;
+    f.lds = lds;
+    f.S = S;
+    f.base = (size_t)bh * S * D;
+    f.lse_base = (size_t)bh * S;
+    f.c = c;
+    f.qsign = qsign;
+    f.tid = threadIdx.x;
+    f.lane = threadIdx.x & 63;
+    f.g = f.lane >> 5;
+    f.n = f.lane & 31;
+    f.rg = (threadIdx.x >> 6) & 1;
+    f.kh = threadIdx.x >> 7;
+
+    // this workgroup's share of the head's K/V rows, pulled into L2 up front
+    const int nwg_head = CAUSAL ? (T + 1) / 2 : T;
+    const int share = (S + nwg_head - 1) / nwg_head;
+    const uint32_t warm = f.warm_l2(p * share, min(S, (p + 1) * share));
+
+    if (CAUSAL) {
+        // the pair (T-1-p, p): heavy tile first, equal total work per workgroup
+        f.run_tile_rows(T - 1 - p);
+        if (p != T - 1 - p) f.run_tile_rows(p);
+    } else {
+        f.run_tile_rows(p);
+    }
+    // keeps the warm-up loads alive; S is never negative
+    if (S < 0 && warm == 0x9e3779b9u) LSE[0] = 0.f;
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a) {
-    using C = Cfg<D>;
-    const int T = (a.S + C::BM - 1) / C::BM;
-    const long long blocks = (long long)a.B * a.H * T;
-    const float c_scale = fabsf(a.scale) * 1.44269504088896340736f;
+    using G = Geo<D>;
+    const int T = (a.S + G::BM - 1) / G::BM;
+    const long long per_head = CAUSAL ? (T + 1) / 2 : T;
+    const long long blocks = (long long)a.B * a.H * per_head;
+    const float c = fabsf(a.scale) * 1.44269504088896340736f;
     const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(C::NT), 0,
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(G::NT), 0,
                        (hipStream_t)a.stream,
                        (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,
-                       (_Float16*)a.o, a.lse, a.B * a.H, a.S, c_scale, qsign);
+                       (_Float16*)a.o, a.lse, a.B * a.H, a.S, c, qsign);
     return hipGetLastError();
 }
 
