@@ -88,7 +88,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   kernel 2: P = softmax rows of S, fp16 [B, H, S, S], and LSE;
  *   kernel 3: O = P V.
  * workspace: device memory of at least attn_fwd_unfused_workspace_bytes(B,H,S)
- * bytes, owned by the caller, overwritten.  Other arguments as attn_fwd.
+ * = B*H*S*Sp*6 bytes (Sp = S rounded up to a multiple of 64: S in fp32 and P
+ * in fp16), owned by the caller, overwritten.  Other arguments as attn_fwd.
+ * Three launches on `stream`, asynchronous like attn_fwd.
  */
 size_t attn_fwd_unfused_workspace_bytes(int B, int H, int S);
 int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o,

@@ -60,8 +60,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 size_t attn_fwd_unfused_workspace_bytes(int B, int H, int S) {
     if (B < 1 || H < 1 || S < 1) return 0;
-    // S as fp32 plus P as fp16, each [B, H, S, S]
-    return (size_t)B * H * S * S * (4 + 2);
+    // S as fp32 plus P as fp16, each [B, H, S, Sp], Sp = S rounded up to 64
+    return (size_t)B * H * S * attn::unfused_row_stride(S) * (4 + 2);
 }
 
 int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o,

@@ -23,5 +23,7 @@ hipError_t launch_fused_d512(const FwdArgs& a);
 // Unfused ablation: QK -> S (fp32, workspace), softmax -> P (fp16, workspace)
 // and LSE, PV -> O.  Three launches on a.stream.
 hipError_t launch_unfused(const FwdArgs& a, void* workspace);
+// Row stride (elements) of the unfused workspace matrices: S rounded up to 64.
+int unfused_row_stride(int S);
 
 }  // namespace attn

@@ -1,4 +1,280 @@
+// Unfused three-kernel attention forward, kept as an ablation of the fused
+// kernels: the same result, but with the n x n intermediates written to and
+// read back from global memory.  It is the three-branch pipeline
+// QK -> softmax -> AV with globally addressed workspaces that "An Optimal
+// Mapper Meets a Real GPU" contrasts with a single fused kernel holding the
+// scores in registers (sections "Ground rules" and "The uncomfortable
+// audit"); for D = 512 the Q K^T kernel runs once per 256-wide head-dim half,
+// the second pass adding into S (option 2 of the STAGE_D.md notes).
+//
+// One decision apart from the fused path: the same MFMA tiles and the same
+// transposed LDS reads of V, only the place where S and P live differs.
+//
+//   qk_kernel      S[b,h,i,j] = scale * q_i . k_j           (fp32, row stride Sp)
+//   softmax_kernel P[b,h,i,j] = exp(S - max) / sum  (fp16),  LSE = max + log(sum)
+//   pv_kernel      O = P V                                  (fp16 out)
+//
+// Workspace: S (fp32) then P (fp16), both [B, H, S, Sp] with Sp = S rounded up
+// to 64, so every row starts 128-byte aligned.  Under causal masking only the
+// entries a later kernel reads are produced: S for j <= i, P up to the next
+// multiple of 128 keys (zeros past the diagonal).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fwd_common.h"
 #include "kernels.h"
+
 namespace attn {
-hipError_t launch_unfused(const FwdArgs&, void*) { return hipErrorNotSupported; }
+namespace {
+
+using namespace detail;
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
+
+// ---------------------------------------------------------------- Q K^T
+
+// One workgroup = 64 queries x 64 keys; wave (wq, wk) a 32 x 32 block.
+// DC head dims starting at d0 are reduced; ACC adds into S instead of writing.
+template <int DC, bool ACC>
+__global__ void __launch_bounds__(256)
+qk_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
+          float* __restrict__ Sm, int S, int Sp, int D, int d0, int causal, float scale)
+{
+    const int TQ = (S + 63) / 64;
+    const int kt = blockIdx.x;
+    const int bh = blockIdx.y / TQ, qt = blockIdx.y % TQ;
+    if (causal && kt > qt) return;  // every key of the block is in the future
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int g = lane >> 5, n = lane & 31;
+    const int wq = w & 1, wk = w >> 1;
+    const size_t base = (size_t)bh * S * D;
+    const int qrow = min(qt * 64 + 32 * wq + n, S - 1);  // A operand row (query)
+    const int krow = min(kt * 64 + 32 * wk + n, S - 1);  // B operand column (key)
+    const _Float16* qp = Q + base + (size_t)qrow * D + d0 + 8 * g;
+    const _Float16* kp = K + base + (size_t)krow * D + d0 + 8 * g;
+    floatx16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll 4
+    for (int kk = 0; kk < DC / 16; ++kk) {
+        const half8 a = *reinterpret_cast<const half8*>(qp + 16 * kk);
+        const half8 b = *reinterpret_cast<const half8*>(kp + 16 * kk);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+    }
+    // C[m = query][n = key]: register r holds query 8(r/4) + 4g + r%4, key n
+    const int j = kt * 64 + 32 * wk + n;
+    if (j >= S) return;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int i = qt * 64 + 32 * wq + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (i < S) {
+            float* dst = Sm + ((size_t)bh * S + i) * Sp + j;
+            const float v = scale * acc[r];
+            *dst = ACC ? *dst + v : v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- softmax
+
+// One wave per row; 4 rows per workgroup.
+__global__ void __launch_bounds__(256)
+softmax_kernel(const float* __restrict__ Sm, _Float16* __restrict__ P, float* __restrict__ LSE,
+               int BHS, int S, int Sp, int causal)
+{
+    const int rowid = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (rowid >= BHS) return;
+    const int lane = threadIdx.x & 63;
+    const int i = rowid % S;
+    const int L = causal ? i + 1 : S;                                  // visible keys
+    // P columns written: the P V kernel reads whole 64-key tiles up to the end
+    // of its query block (at most 128 rows), so past the diagonal write zeros
+    // up to the next multiple of 128.
+    const int Lp = causal ? min(Sp, ((i + 128) / 128) * 128) : Sp;
+    const float* srow = Sm + (size_t)rowid * Sp;
+    _Float16* prow = P + (size_t)rowid * Sp;
+    // per-lane running max and sum (base-2), then a wave reduction
+    float m = kNegInf, l = 0.f;
+    for (int j = lane; j < L; j += 64) {
+        const float x = srow[j] * kLog2e;
+        const float mn = fmaxf(m, x);
+        l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(x - mn);
+        m = mn;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float mo = __shfl_xor(m, off, 64), lo = __shfl_xor(l, off, 64);
+        const float mn = fmaxf(m, mo);
+        l = (mn == kNegInf) ? 0.f
+                            : l * __builtin_amdgcn_exp2f(m - mn) + lo * __builtin_amdgcn_exp2f(mo - mn);
+        m = mn;
+    }
+    const float inv = 1.0f / l;
+    for (int j = lane; j < Lp; j += 64) {
+        const float p = j < L ? __builtin_amdgcn_exp2f(srow[j] * kLog2e - m) * inv : 0.f;
+        prow[j] = (_Float16)p;
+    }
+    if (lane == 0) LSE[rowid] = (m + __builtin_amdgcn_logf(l)) * kLn2;
+}
+
+// ---------------------------------------------------------------- P V
+
+template <int D>
+struct PvGeo {
+    static constexpr int DW = D < 128 ? D : 128;   // output dims per wave
+    static constexpr int DQ = D / DW;              // waves sharing a query group
+    static constexpr int QG = 4 / DQ;              // 32-query groups per workgroup
+    static constexpr int BM = 32 * QG;             // queries per workgroup
+    static constexpr int BN = 64;                  // keys per tile
+    static constexpr int CPR = D / 8;
+    static constexpr int CH = BN * CPR / 256;      // V chunks per thread per tile
+    static_assert(DQ * QG == 4, "4 waves");
+};
+
+template <int D>
+__device__ __forceinline__ int swz_pv(int r) {
+    return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 1)
+pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float16* __restrict__ O,
+          int S, int Sp, int causal)
+{
+    using G = PvGeo<D>;
+    __shared__ __attribute__((aligned(1024))) _Float16 vs[G::BN * D];
+    const int TQ = (S + G::BM - 1) / G::BM;
+    const int bh = blockIdx.x / TQ, qt = blockIdx.x % TQ;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int g = lane >> 5, n = lane & 31;
+    const int qg = w / G::DQ, dq = w % G::DQ;
+    const int q0 = qt * G::BM;
+    const int qrow = q0 + 32 * qg + n;
+    const size_t vbase = (size_t)bh * S * D;
+    const _Float16* prow = P + ((size_t)bh * S + min(qrow, S - 1)) * Sp + 8 * g;
+    const int kend = causal ? min(S, q0 + G::BM) : S;
+    const int nT = (kend + G::BN - 1) / G::BN;
+
+    floatx16 o[G::DW / 32];
+#pragma unroll
+    for (int b = 0; b < G::DW / 32; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
+
+    u32x4 st[G::CH];
+    auto load = [&](int t) {
+        const int j0 = t * G::BN;
+        const auto r = rsrc(V + vbase + (size_t)j0 * D, (uint32_t)(S - j0) * D * 2);
+#pragma unroll
+        for (int u = 0; u < G::CH; ++u)
+            st[u] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (tid + 256 * u), 0, 0));
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int u = 0; u < G::CH; ++u) {
+            const int ci = tid + 256 * u, row = ci / G::CPR, cc = ci % G::CPR;
+            *reinterpret_cast<u32x4*>(vs + row * D + 8 * (cc ^ swz_pv<D>(row))) = st[u];
+        }
+    };
+
+    const int n16 = n >> 4, jj = n & 15;
+    const int sub = (jj & 3) >> 1, half = jj & 1;
+    const int sw = swz_pv<D>(jj >> 2);  // (row & 3) == jj >> 2 for every row read
+    load(0);
+    for (int t = 0; t < nT; ++t) {
+        store();
+        barrier();
+        if (t + 1 < nT) load(t + 1);
+        // transposed reads deliver keys 16ks + 8g + 4tt + 0..3: the lane's 8 keys
+        // are contiguous, matching a 16-byte load of its P row
+        const _Float16* rowp = vs + (8 * g + (jj >> 2)) * D + 4 * half;
+#pragma unroll
+        for (int ks = 0; ks < G::BN / 16; ++ks) {
+            // P^T operand: this lane's query, keys j0 + 16ks + 8g .. +7
+            const half8 pf = *reinterpret_cast<const half8*>(prow + t * G::BN + 16 * ks);
+#pragma unroll
+            for (int b = 0; b < G::DW / 32; ++b) {
+                const int logical = (G::DW * dq) / 8 + 4 * b + 2 * n16 + sub;
+                const _Float16* pb = rowp + 8 * (logical ^ sw) + 16 * ks * D;
+                half4 part[2];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+                    part[tt] = __builtin_bit_cast(
+                        half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_half4*)(pb + 4 * tt * D)));
+                const half8 a = {part[0][0], part[0][1], part[0][2], part[0][3],
+                                 part[1][0], part[1][1], part[1][2], part[1][3]};
+                o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf, o[b], 0, 0, 0);
+            }
+        }
+        barrier();
+    }
+    if (qrow < S) {
+        _Float16* orow = O + vbase + (size_t)qrow * D + G::DW * dq;
+#pragma unroll
+        for (int b = 0; b < G::DW / 32; ++b)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                u32x2 pk;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const _Float16 lo = (_Float16)o[b][4 * q4 + 2 * h];
+                    const _Float16 hi = (_Float16)o[b][4 * q4 + 2 * h + 1];
+                    pk[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+                }
+                *reinterpret_cast<u32x2*>(orow + 32 * b + 8 * q4 + 4 * g) = pk;
+            }
+    }
+}
+
+template <int D>
+hipError_t launch_pv(const FwdArgs& a, const _Float16* P, int Sp) {
+    using G = PvGeo<D>;
+    const int TQ = (a.S + G::BM - 1) / G::BM;
+    hipLaunchKernelGGL(pv_kernel<D>, dim3((unsigned)(a.B * a.H * TQ)), dim3(256), 0,
+                       (hipStream_t)a.stream, P, (const _Float16*)a.v, (_Float16*)a.o, a.S, Sp,
+                       a.causal);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int unfused_row_stride(int S) { return (S + 63) / 64 * 64; }
+
+hipError_t launch_unfused(const FwdArgs& a, void* workspace) {
+    const int S = a.S, Sp = unfused_row_stride(S);
+    const int BH = a.B * a.H;
+    float* Sm = reinterpret_cast<float*>(workspace);
+    _Float16* P = reinterpret_cast<_Float16*>(Sm + (size_t)BH * S * Sp);
+    const int TQ = (S + 63) / 64;
+    const dim3 qk_grid((unsigned)TQ, (unsigned)(BH * TQ));
+    const hipStream_t st = (hipStream_t)a.stream;
+    const _Float16* q = (const _Float16*)a.q;
+    const _Float16* k = (const _Float16*)a.k;
+    if (a.D == 64)
+        hipLaunchKernelGGL((qk_kernel<64, false>), qk_grid, dim3(256), 0, st, q, k, Sm, S, Sp, 64, 0, a.causal, a.scale);
+    else if (a.D == 128)
+        hipLaunchKernelGGL((qk_kernel<128, false>), qk_grid, dim3(256), 0, st, q, k, Sm, S, Sp, 128, 0, a.causal, a.scale);
+    else {
+        // two head-dim sub-tiles, summed into S before the softmax
+        hipLaunchKernelGGL((qk_kernel<256, false>), qk_grid, dim3(256), 0, st, q, k, Sm, S, Sp, 512, 0, a.causal, a.scale);
+        hipLaunchKernelGGL((qk_kernel<256, true>), qk_grid, dim3(256), 0, st, q, k, Sm, S, Sp, 512, 256, a.causal, a.scale);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int BHS = BH * S;
+    hipLaunchKernelGGL(softmax_kernel, dim3((unsigned)((BHS + 3) / 4)), dim3(256), 0, st, Sm, P, a.lse,
+                       BHS, S, Sp, a.causal);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.D == 64) return launch_pv<64>(a, P, Sp);
+    if (a.D == 128) return launch_pv<128>(a, P, Sp);
+    return launch_pv<512>(a, P, Sp);
+}
+
+}  // namespace attn

@@ -80,7 +80,7 @@ def test_fused_validation(L, kw, code):
 
 def test_unfused_validation(L):
     need = L.attn_fwd_unfused_workspace_bytes(2, 3, 100)
-    assert need == 2 * 3 * 100 * 100 * 6
+    assert need == 2 * 3 * 100 * 128 * 6  # rows padded to 128 (a multiple of 64)
     assert L.attn_fwd_unfused_workspace_bytes(0, 3, 100) == 0
     W = 0x90000000
     args = (Q, K, V, O, LSE, 2, 3, 100, 128, 1, 0.1)
