@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=3.0,
                    help="minimum wall time of the oracle timing loop")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of this many MiB (the reference "
+                        "kernel for scaling HBM byte counters) and exit")
     return p.parse_args()
 
 
@@ -83,6 +86,27 @@ def cpu_baseline(w, min_seconds):
                       f"{reps} calls"}
 
 
+def measured_traffic(workload_name, path):
+    """HBM bytes per launch from the committed PMC summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by the same counter on a plain copy of known size),
+    or None when no summary covers this workload or the kernel sources have
+    changed since the counters were taken."""
+    import glob
+    import hashlib
+    if path != "fused":
+        return None
+    for fn in glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json")):
+        with open(fn) as f:
+            t = json.load(f)
+        if t.get("workload") != workload_name:
+            continue
+        h = hashlib.sha256(b"".join(open(os.path.join(ROOT, s), "rb").read()
+                                    for s in t["kernel_sources"])).hexdigest()
+        if h == t["kernel_source_sha256"]:
+            return t["traffic_bytes_per_launch"]
+    return None
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -92,6 +116,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_(0, 255)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 10}))
+        return
     import scaled_dot_product_attn_amd as attn
     from scaled_dot_product_attn_amd import inputs
 
@@ -164,6 +197,7 @@ def main():
         gbs = nbytes / (mean_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": gbs / PEAK_HBM_GBS, "traffic": None}
+    roof["traffic"] = measured_traffic(w.name, args.path)
     roof["kernel_mean_us"] = mean_us
     roof["per_launch"] = {"flops": flops, "alg_bytes": nbytes}
 
