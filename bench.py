@@ -100,8 +100,11 @@ def measured_traffic(workload_name, path):
             t = json.load(f)
         if t.get("workload") != workload_name:
             continue
-        h = hashlib.sha256(b"".join(open(os.path.join(ROOT, s), "rb").read()
-                                    for s in t["kernel_sources"])).hexdigest()
+        try:
+            h = hashlib.sha256(b"".join(open(os.path.join(ROOT, s), "rb").read()
+                                        for s in t["kernel_sources"])).hexdigest()
+        except OSError:  # a source the counters were taken on is gone
+            continue
         if h == t["kernel_source_sha256"]:
             return t["traffic_bytes_per_launch"]
     return None

@@ -16,8 +16,9 @@ struct FwdArgs {
     void* stream;
 };
 
-// Fused single-kernel forward, D = 64 or 128.
-hipError_t launch_fused_d64_d128(const FwdArgs& a);
+// Fused single-kernel forward, D = 64 or 128: two query tiles per workgroup
+// of eight waves (causal pairs t, T-1-t).
+hipError_t launch_fused_pair8_d64_d128(const FwdArgs& a);
 // Fused single-kernel forward, D = 512 (head-dim halves summed in logit space).
 hipError_t launch_fused_d512(const FwdArgs& a);
 // Unfused ablation: QK -> S (fp32, workspace), softmax -> P (fp16, workspace)

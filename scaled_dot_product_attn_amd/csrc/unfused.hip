@@ -48,7 +48,7 @@ qk_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     const int kt = blockIdx.x;
     const int bh = blockIdx.y / TQ, qt = blockIdx.y % TQ;
     if (causal && kt > qt) return;  // every key of the block is in the future
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int g = lane >> 5, n = lane & 31;
     const int wq = w & 1, wk = w >> 1;
     const size_t base = (size_t)bh * S * D;
@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(256)
 softmax_kernel(const float* __restrict__ Sm, _Float16* __restrict__ P, float* __restrict__ LSE,
                int BHS, int S, int Sp, int causal)
 {
-    const int rowid = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int rowid = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (rowid >= BHS) return;
     const int lane = threadIdx.x & 63;
     const int i = rowid % S;
@@ -149,7 +149,7 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
     __shared__ __attribute__((aligned(1024))) _Float16 vs[G::BN * D];
     const int TQ = (S + G::BM - 1) / G::BM;
     const int bh = blockIdx.x / TQ, qt = blockIdx.x % TQ;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 5, n = lane & 31;
     const int qg = w / G::DQ, dq = w % G::DQ;
     const int q0 = qt * G::BM;
