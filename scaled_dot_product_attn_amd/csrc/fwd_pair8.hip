@@ -204,32 +204,37 @@ struct Fwd8 {
                 o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[h][b], pf[h], o[b], 0, 0, 0);
     }
 
-    // This wave's 32 x 32 block of key tile j at t.
+    // First half of this wave's 32 x 32 block of key tile j at t: S = Q K^T,
+    // online softmax -> P (pf), and the V^T fragments for the second half.
     template <bool MASK>
-    __device__ __forceinline__ void block(const _Float16* t, int j, int row, const half8* qf,
-                                          float& m, float& l, floatx16* o) const {
+    __device__ __forceinline__ void block_qk(const _Float16* t, int j, int row, const half8* qf,
+                                             float& m, float& l, floatx16* o, half8* pf,
+                                             half8 (*vf)[NB]) const {
         half8 kf[D / 16];
         read_k(kf, t);
-        half8 vf[2][NB];
         read_v(vf, t);
         const floatx16 s = qk(kf, qf);
-        half8 pf[2];
         // visibility: key <= min(row, S-1) (causal) or key <= S-1
         const int lim = (CAUSAL ? min(row, S - 1) : S - 1) - (j * G::BN + 32 * kh + 4 * g);
         online_softmax<MASK, NB>(s, lim, c, m, l, o, pf);
-        pv(o, vf, pf);
     }
 
-    // One step: next tiles -> registers, this wave's block (if any), next
-    // tiles -> the other stage.
+    // One step: next tiles -> registers; this wave's block (if any), with the
+    // next tiles written to the other stage between its softmax and its P V
+    // so that the LDS writes overlap the matrix work.
     template <bool MASK>
     __device__ __forceinline__ void step(int stg, int jnext, int cnext, bool active, int slot,
                                          int j, int row, const half8* qf, float& m, float& l,
                                          floatx16* o) {
         barrier();  // this step's tiles are in LDS; every wave is done with the last step
         load_next(jnext, cnext);
-        if (active) block<MASK>(lds + stg * G::STAGE + slot * G::TILE, j, row, qf, m, l, o);
+        half8 pf[2];
+        half8 vf[2][NB];
+        if (active) block_qk<MASK>(lds + stg * G::STAGE + slot * G::TILE, j, row, qf, m, l, o, pf, vf);
+        // stage stg^1 held the previous step's tiles, which every wave has
+        // finished with (barrier above)
         store_next(stg ^ 1, cnext);
+        if (active) pv(o, vf, pf);
     }
 
     __device__ __forceinline__ void load_q(half8* qf, int row) const {
@@ -245,11 +250,15 @@ struct Fwd8 {
 
     // Partial-state exchange through LDS at float offset `at`: slot q holds a
     // wave's O^T as float4 [b][q4][lane], then m and l [lane].
-    __device__ __forceinline__ void publish(float* at, int q, const floatx16* o, float m,
+    // Only the blocks that other members of a merge group of GS waves combine
+    // (b % GS != gidx) are written.
+    template <int GS>
+    __device__ __forceinline__ void publish(float* at, int q, int gidx, const floatx16* o, float m,
                                             float l) const {
         float4* mo = reinterpret_cast<float4*>(at + q * (G::PART + 128));
 #pragma unroll
         for (int b = 0; b < NB; ++b)
+            if (b % GS != gidx)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4)
                 mo[(4 * b + q4) * 64 + lane] =
@@ -384,7 +393,7 @@ struct Fwd8 {
             // partial state for b's rows.
             barrier();
             float* at = reinterpret_cast<float*>(lds + (stg ^ 1) * G::STAGE);
-            if (hi == 0) publish(at, w, o, m, l);
+            if (hi == 0) publish<2>(at, w, kh, o, m, l);
             barrier();
             if (hi == 0) {
                 const int other[1] = {w ^ 2};
@@ -420,7 +429,10 @@ struct Fwd8 {
         // the two key halves of a's rows and of b's rows.
         barrier();  // every wave is done reading the stages
         float* at = reinterpret_cast<float*>(lds);
-        publish(at, w, o, m, l);
+        if (n2 > 0)
+            publish<4>(at, w, w >> 1, o, m, l);
+        else
+            publish<2>(at, w, kh, o, m, l);
         barrier();
         if (n2 > 0) {
             const int other[3] = {w ^ 2, w ^ 4, w ^ 6};
