@@ -52,7 +52,9 @@ def parse():
                    help="1..5 (default 3: B=1 H=32 S=1024 D=128 causal)")
     p.add_argument("--rotate", type=int, default=1,
                    help="cycle through this many independent input sets")
-    p.add_argument("--path", choices=["fused", "unfused"], default="fused")
+    p.add_argument("--path", choices=["fused", "unfused", "splitkv"], default="fused")
+    p.add_argument("--splits", type=int, default=3,
+                   help="split-KV path: chunks of the longest key range (D = 512 only)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=3.0,
                    help="minimum wall time of the oracle timing loop")
@@ -148,14 +150,20 @@ def main():
     if args.path == "unfused":
         ws = torch.empty(attn.unfused_workspace_bytes(w.B, w.H, w.S), dtype=torch.uint8,
                          device=dev)
+    elif args.path == "splitkv":
+        nbytes = attn.splitkv_workspace_bytes(w.B, w.H, w.S, w.D, w.causal, args.splits)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
 
     def step(i):
         q, k, v = sets[i % len(sets)]
-        if ws is None:
+        if args.path == "fused":
             attn.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
-        else:
+        elif args.path == "unfused":
             attn.fwd_unfused(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse,
                              workspace=ws)
+        else:
+            attn.fwd_splitkv(q, k, v, causal=w.causal, scale=w.scale, splits=args.splits,
+                             out=o, lse=lse, workspace=ws)
 
     stream = torch.cuda.current_stream(dev)  # the stream attn.fwd launches on
     for i in range(args.warmup):
@@ -220,6 +228,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
                    "causal": w.causal, "scale": w.scale, "sigma": w.sigma,
                    "path": args.path, "input_sets": args.rotate,
+                   **({"splits": args.splits} if args.path == "splitkv" else {}),
                    "cache": "warm (same buffers)" if args.rotate == 1 else
                             f"rotating {args.rotate} input sets"},
         "us_per_call": {"mean": mean_us, "median": med_us, "p10": p10, "p90": p90,

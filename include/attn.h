@@ -64,6 +64,7 @@ extern "C" {
 #define ATTN_ERR_LAUNCH -5    /* the HIP launch failed (see attn_last_hip_error) */
 #define ATTN_ERR_WORKSPACE -6 /* workspace NULL or smaller than required */
 #define ATTN_ERR_ALIAS -7     /* an output buffer overlaps another buffer */
+#define ATTN_ERR_SPLITS -8    /* splits < 1 */
 
 /*
  * Fused forward: one kernel, scores kept on chip.
@@ -97,6 +98,35 @@ int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o,
                      float* lse, int B, int H, int S, int D, int causal,
                      float scale, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * Split-KV forward for head dimension 512, for shapes with few (batch, head)
+ * slices and long causal rows, where one workgroup per query tile leaves most
+ * of the GPU idle.  The key range of every 64-row query tile is cut into
+ * chunks of at most C = ceil(ceil(S/32) / splits) 32-key tiles; each chunk is
+ * one workgroup that leaves its partial state (unnormalised O in fp32, row
+ * max and row sum) in `workspace`, and a second kernel merges the chunks of
+ * each row in chunk order (deterministic).  The merge over DISJOINT key sets
+ * is exact up to rounding (STAGE_D.md notes, section "2. External k_sub Merge
+ * is Mathematically Impossible": outputs over different token sets combine
+ * through their weights); the partial write, re-read and reduction are the
+ * split-k costs that "An Optimal Mapper Meets a Real GPU" (section
+ * "Experiment one: ten mappings, forty handwritten kernels") says must be
+ * paid.  Query tiles with a single chunk are written directly; splits = 1
+ * gives the fused result bit for bit.
+ *   D         : must be 512 (else ATTN_ERR_HEAD_DIM)
+ *   splits    : >= 1 (else ATTN_ERR_SPLITS)
+ *   workspace : device memory of at least
+ *               attn_fwd_splitkv_workspace_bytes(B, H, S, D, causal, splits)
+ *               bytes, owned by the caller and overwritten; may be NULL when
+ *               that size is 0 (no query tile is split).
+ * Other arguments as attn_fwd.  One or two launches on `stream`,
+ * asynchronous like attn_fwd.
+ */
+size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int S, int D, int causal, int splits);
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int S, int D, int causal, float scale, int splits,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* 1 if attn_fwd accepts head dimension D, else 0. */
 int attn_head_dim_supported(int D);

@@ -13,11 +13,13 @@ import os
 
 from .build import LIB_PATH
 
-__all__ = ["AttnError", "fwd", "fwd_unfused", "unfused_workspace_bytes",
-           "head_dim_supported", "load_library", "LIB_PATH", "SYMBOLS"]
+__all__ = ["AttnError", "fwd", "fwd_unfused", "unfused_workspace_bytes", "fwd_splitkv",
+           "splitkv_workspace_bytes", "head_dim_supported", "load_library", "LIB_PATH",
+           "SYMBOLS"]
 
 # Every symbol include/attn.h declares.
 SYMBOLS = ("attn_fwd", "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
+           "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
            "attn_head_dim_supported", "attn_status_string", "attn_last_hip_error")
 
 ATTN_ERR_LAUNCH = -5
@@ -56,6 +58,10 @@ def load_library(path: str = LIB_PATH):
     L.attn_fwd_unfused.restype = I
     L.attn_fwd_unfused_workspace_bytes.argtypes = [I, I, I]
     L.attn_fwd_unfused_workspace_bytes.restype = Z
+    L.attn_fwd_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, Z, P]
+    L.attn_fwd_splitkv.restype = I
+    L.attn_fwd_splitkv_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    L.attn_fwd_splitkv_workspace_bytes.restype = Z
     L.attn_head_dim_supported.argtypes = [I]
     L.attn_head_dim_supported.restype = I
     L.attn_status_string.argtypes = [I]
@@ -143,4 +149,29 @@ def fwd_unfused(q, k, v, *, causal: bool, scale: float | None = None, out=None,
                               lse.data_ptr(), B, H, S, D, int(bool(causal)), scale,
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                               stream))
+    return out, lse
+
+
+def splitkv_workspace_bytes(B: int, H: int, S: int, D: int, causal: bool, splits: int) -> int:
+    return int(load_library().attn_fwd_splitkv_workspace_bytes(B, H, S, D, int(bool(causal)),
+                                                                splits))
+
+
+def fwd_splitkv(q, k, v, *, causal: bool, splits: int = 4, scale: float | None = None,
+                out=None, lse=None, workspace=None):
+    """Split-KV forward (D = 512): every query tile's key range in chunks of
+    at most ceil(ceil(S/32) / splits) 32-key tiles, merged in chunk order.
+    ``workspace``: a uint8 GPU tensor of at least splitkv_workspace_bytes(...)
+    bytes; allocated with torch when not given and needed."""
+    import torch
+    L = load_library()
+    B, H, S, D, out, lse, scale, stream = _prepare(q, k, v, out, lse, scale)
+    need = splitkv_workspace_bytes(B, H, S, D, causal, splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(L.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), B, H, S, D, int(bool(causal)), scale, int(splits),
+                              wptr, wbytes, stream))
     return out, lse

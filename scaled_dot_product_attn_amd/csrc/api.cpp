@@ -81,6 +81,37 @@ int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o,
     return launched(attn::launch_unfused(a, workspace));
 }
 
+size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int S, int D, int causal, int splits) {
+    if (B < 1 || H < 1 || S < 1 || D != 512 || splits < 1) return 0;
+    const int T = (S + 63) / 64;
+    if (attn::splitkv_d512_units(S, causal != 0, splits) == T) return 0;  // nothing is split
+    return attn::splitkv_d512_workspace_floats(B, H, S, causal != 0, splits) * sizeof(float);
+}
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int S, int D, int causal, float scale, int splits,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    const int st = validate(q, k, v, o, lse, B, H, S, D, scale);
+    if (st != ATTN_OK) return st;
+    if (D != 512) return ATTN_ERR_HEAD_DIM;
+    if (splits < 1) return ATTN_ERR_SPLITS;
+    // one workgroup per (batch, head, work unit), and per 8 rows in the merge
+    if ((long long)B * H * attn::splitkv_d512_units(S, causal != 0, splits) > INT32_MAX ||
+        (long long)B * H * ((S + 63) / 64) * 8 > INT32_MAX)
+        return ATTN_ERR_SHAPE;
+    const size_t need = attn_fwd_splitkv_workspace_bytes(B, H, S, D, causal, splits);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+        const size_t nt = (size_t)B * H * S * D * 2, nl = (size_t)B * H * S * 4;
+        if (overlaps(workspace, need, q, nt) || overlaps(workspace, need, k, nt) ||
+            overlaps(workspace, need, v, nt) || overlaps(workspace, need, o, nt) ||
+            overlaps(workspace, need, lse, nl))
+            return ATTN_ERR_ALIAS;
+    }
+    const attn::FwdArgs a{q, k, v, o, lse, B, H, S, D, causal != 0, scale, stream};
+    return launched(attn::launch_splitkv_d512(a, splits, need > 0 ? workspace : nullptr));
+}
+
 const char* attn_status_string(int status) {
     switch (status) {
         case ATTN_OK: return "ok";
@@ -91,6 +122,7 @@ const char* attn_status_string(int status) {
         case ATTN_ERR_LAUNCH: return "HIP kernel launch failed (see attn_last_hip_error)";
         case ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_fwd_unfused_workspace_bytes";
         case ATTN_ERR_ALIAS: return "an output buffer overlaps another buffer";
+        case ATTN_ERR_SPLITS: return "splits must be >= 1";
         default: return "unknown status";
     }
 }

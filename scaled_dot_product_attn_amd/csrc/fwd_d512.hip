@@ -23,6 +23,22 @@
 //     pv_n_tile knob; it keeps a wave's output accumulator at 128 registers.
 //   * K (padded rows) and V (XOR-swizzled rows) stream through two LDS stages,
 //     staged through registers with bounds-checked buffer loads.
+//
+// Split-KV.  Eight heads of 1024 rows give only 128 workgroups for 256 CUs, and
+// under causal masking the last query tile does 32 key tiles while the first
+// does 2.  The split variant cuts every query tile's key range into chunks of
+// at most C 32-key tiles; each chunk is one workgroup that leaves its partial
+// state (unnormalised O in fp32, row max m and row sum l) in a workspace, and
+// a second kernel merges the chunks of a row in chunk order.  The merge is
+// exact because the chunks hold DISJOINT key sets (STAGE_D.md notes, section
+// "2. External k_sub Merge is Mathematically Impossible": outputs over
+// different token sets combine through their weights, unlike head-dim
+// sub-tiles); the partial write, re-read and reduction are the split-k costs
+// that "An Optimal Mapper Meets a Real GPU" (section "Experiment one: ten
+// mappings, forty handwritten kernels", cost term (1)) says must be paid and
+// measured.  Query tiles with a single chunk write O and LSE directly.  The
+// fused entry point is the same kernel with C = every key tile (one chunk per
+// query tile, heaviest first).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -153,12 +169,13 @@ struct Fwd512 {
         }
     }
 
-    __device__ void run(int qt) {
+    // Query tile qt over key tiles [kt0, kt1).  part == nullptr: write O and
+    // LSE; otherwise leave the partial state in the chunk's workspace slot:
+    // unnormalised O as fp32 [64][512], then m[64] (log2 units) and l[64].
+    __device__ void run(int qt, int kt0, int kt1, float* part) {
         const int q0 = qt * G::BM;
         const int row = q0 + 32 * rg + n;
         const int r_lo = q0 + 32 * rg, r_hi = r_lo + 31;
-        const int kv_end = causal ? min(S, q0 + G::BM) : S;
-        const int nT = (kv_end + G::BN - 1) / G::BN;
 
         // Q^T fragment of this wave's rows and head-dim half.
         half8 qf[G::DH / 16];
@@ -180,27 +197,28 @@ struct Fwd512 {
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
 
-        load_part<false>(0);
+        load_part<false>(kt0);
         store_part<false>(0);
-        load_part<true>(0);
+        load_part<true>(kt0);
         store_part<true>(0);
         barrier();
         float* mine = xch + w * 16 * 64;
         const float* other = xch + (w ^ 2) * 16 * 64;  // same row group, other half
-        for (int i = 0; i < nT; ++i) {
+        for (int i = kt0; i < kt1; ++i) {
+            const int li = i - kt0;  // LDS stage of tile i: li & 1
             const int j0 = i * G::BN;
-            const int jn = min(i + 1, nT - 1);  // past the end: reload the last tile
+            const int jn = min(i + 1, kt1 - 1);  // past the end: reload the last tile
             load_part<false>(jn);
             const bool skip = causal && j0 > r_hi;  // every key is in this wave's future
             floatx16 s;
             if (!skip) {
-                s = qk_half(qf, i & 1);
+                s = qk_half(qf, li & 1);
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
                     *reinterpret_cast<float4*>(mine + (4 * q4) * 64 + 4 * lane) =
                         float4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
             }
-            store_part<false>((i + 1) & 1);  // stage of tile i-1, free since the last barrier
+            store_part<false>((li + 1) & 1);  // stage of tile i-1, free since the last barrier
             load_part<true>(jn);
             barrier();  // both sub-tile partials are published
             if (!skip) {
@@ -220,15 +238,29 @@ struct Fwd512 {
                     online_softmax<true, G::DH / 32>(s, lim, c, m, l, o, pf);
                 else
                     online_softmax<false, G::DH / 32>(s, lim, c, m, l, o, pf);
-                pv_half(o, pf, i & 1);
+                pv_half(o, pf, li & 1);
             }
-            store_part<true>((i + 1) & 1);
+            store_part<true>((li + 1) & 1);
             barrier();  // next tile in LDS; exchange buffer free again
         }
 
         // Epilogue: both waves of a row group hold the same m and l; each
         // writes its 256 output dims.
         const float lt = sum_halves(l);
+        if (part) {
+            float* po = part + (size_t)(32 * rg + n) * G::D + G::DH * dh;
+#pragma unroll
+            for (int b = 0; b < G::DH / 32; ++b)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    *reinterpret_cast<float4*>(po + 32 * b + 8 * q4 + 4 * g) =
+                        float4{o[b][4 * q4], o[b][4 * q4 + 1], o[b][4 * q4 + 2], o[b][4 * q4 + 3]};
+            if (dh == 0 && g == 0) {
+                part[G::BM * G::D + 32 * rg + n] = m;
+                part[G::BM * G::D + G::BM + 32 * rg + n] = lt;
+            }
+            return;
+        }
         const float inv = 1.0f / lt;
         if (row < S) {
             _Float16* orow = O + base + (size_t)row * G::D + G::DH * dh;
@@ -251,18 +283,56 @@ struct Fwd512 {
     }
 };
 
+// Chunking of the key range.  Query tile qt sees nkt(qt) 32-key tiles and is
+// cut into nchunks(qt) chunks of at most C tiles.  Work units enumerate
+// (query tile, chunk) heaviest tile first; a unit's partial-state slot is
+// (bh * U + unit).
+struct Chunking {
+    int S, T, C, causal;
+    __host__ __device__ int nkt(int qt) const {
+        const int kv_end = causal ? min(S, (qt + 1) * G512::BM) : S;
+        return (kv_end + G512::BN - 1) / G512::BN;
+    }
+    __host__ __device__ int nchunks(int qt) const { return (nkt(qt) + C - 1) / C; }
+    __host__ __device__ int units() const {
+        int u = 0;
+        for (int qt = 0; qt < T; ++qt) u += nchunks(qt);
+        return u;
+    }
+    // unit u -> (query tile, chunk)
+    __host__ __device__ void decode(int u, int& qt, int& chunk) const {
+        for (qt = T - 1; qt > 0; --qt) {
+            const int c = nchunks(qt);
+            if (u < c) break;
+            u -= c;
+        }
+        chunk = u;
+    }
+    __host__ __device__ int first_unit(int qt) const {
+        int u = 0;
+        for (int q = T - 1; q > qt; --q) u += nchunks(q);
+        return u;
+    }
+};
+
+constexpr size_t kSlotFloats = (size_t)G512::BM * G512::D + 2 * G512::BM;
+
 __global__ void __launch_bounds__(256, 1)
 fwd512_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
               const _Float16* __restrict__ V, _Float16* __restrict__ O,
-              float* __restrict__ LSE, int BH, int S, int causal, float c, uint32_t qsign)
+              float* __restrict__ LSE, int BH, int S, int causal, float c, uint32_t qsign,
+              Chunking ch, int U, float* __restrict__ ws)
 {
     using G = G512;
     __shared__ __attribute__((aligned(1024))) _Float16 lds[G::NS * G::STAGE + 2 * G::XCH];
 
-    const int T = (S + G::BM - 1) / G::BM;
     const int bh = blockIdx.x % BH;
-    int qt = blockIdx.x / BH;
-    if (causal) qt = T - 1 - qt;  // longest rows first
+    const int unit = blockIdx.x / BH;
+    int qt, chunk;
+    ch.decode(unit, qt, chunk);
+    const int n = ch.nkt(qt);
+    const int kt0 = chunk * ch.C, kt1 = min(n, kt0 + ch.C);
+    float* part = ch.nchunks(qt) > 1 ? ws + ((size_t)bh * U + unit) * kSlotFloats : nullptr;
 
     Fwd512 f;
     f.Q = Q;
@@ -285,24 +355,112 @@ fwd512_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     f.n = f.lane & 31;
     f.rg = f.w & 1;
     f.dh = f.w >> 1;
-    f.run(qt);
+    f.run(qt, kt0, kt1, part);
 }
 
-hipError_t launch(const FwdArgs& a) {
+// Merge the chunks of one query tile's rows in chunk order: with
+// m* = max_c m_c and w_c = 2^(m_c - m*), O = sum_c w_c O_c / sum_c w_c l_c and
+// LSE = (m* + log2 sum_c w_c l_c) ln 2.  A workgroup takes 8 rows of one query
+// tile; 32 threads share a row, each owning 16 consecutive head dims, so the
+// partial outputs are read as contiguous 2 KB rows.
+constexpr int kMergeRows = 8;
+
+__global__ void __launch_bounds__(256)
+merge512_kernel(const float* __restrict__ ws, _Float16* __restrict__ O, float* __restrict__ LSE,
+                int BH, int S, Chunking ch, int U)
+{
     using G = G512;
-    const int T = (a.S + G::BM - 1) / G::BM;
-    const long long blocks = (long long)a.B * a.H * T;
+    const int per_tile = G::BM / kMergeRows;
+    const int bh = blockIdx.x % BH;
+    const int rest = blockIdx.x / BH;
+    const int qt = rest / per_tile, rb = rest % per_tile;
+    const int nch = ch.nchunks(qt);
+    if (nch <= 1) return;  // written directly by the first kernel
+    const float* slot0 = ws + ((size_t)bh * U + ch.first_unit(qt)) * kSlotFloats;
+    const int r = rb * kMergeRows + (threadIdx.x >> 5);  // row within the query tile
+    const int d0 = 16 * (threadIdx.x & 31);
+    const int row = qt * G::BM + r;
+    float mt = kNegInf;
+    for (int cc = 0; cc < nch; ++cc) mt = fmaxf(mt, slot0[cc * kSlotFloats + G::BM * G::D + r]);
+    float lsum = 0.f;
+    float4 acc[4] = {};
+    for (int cc = 0; cc < nch; ++cc) {
+        const float* sl = slot0 + cc * kSlotFloats;
+        // a chunk that saw no key of this row has l = 0 and zero O
+        const float wgt = __builtin_amdgcn_exp2f(sl[G::BM * G::D + r] - mt);
+        lsum += wgt * sl[G::BM * G::D + G::BM + r];
+        const float4* x = reinterpret_cast<const float4*>(sl + (size_t)r * G::D + d0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float4 y = x[e];
+            acc[e].x += wgt * y.x;
+            acc[e].y += wgt * y.y;
+            acc[e].z += wgt * y.z;
+            acc[e].w += wgt * y.w;
+        }
+    }
+    if (row >= S) return;
+    const float inv = 1.0f / lsum;
+    u32x4 pk[2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        pk[e >> 1][2 * (e & 1)] =
+            (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(acc[e].x * inv)) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(acc[e].y * inv)) << 16);
+        pk[e >> 1][2 * (e & 1) + 1] =
+            (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(acc[e].z * inv)) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(acc[e].w * inv)) << 16);
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(O + ((size_t)bh * S + row) * G::D + d0);
+    dst[0] = pk[0];
+    dst[1] = pk[1];
+    if (d0 == 0) LSE[(size_t)bh * S + row] = (mt + __builtin_amdgcn_logf(lsum)) * kLn2;
+}
+
+Chunking make_chunking(int S, int causal, int splits) {
+    Chunking ch;
+    ch.S = S;
+    ch.T = (S + G512::BM - 1) / G512::BM;
+    ch.causal = causal;
+    const int nmax = (S + G512::BN - 1) / G512::BN;  // key tiles of the longest row
+    ch.C = splits <= 0 ? nmax : (nmax + splits - 1) / splits;
+    return ch;
+}
+
+hipError_t launch(const FwdArgs& a, int splits, float* ws) {
+    using G = G512;
+    const Chunking ch = make_chunking(a.S, a.causal, splits);
+    const int U = ch.units();
+    const int BH = a.B * a.H;
     const float c = fabsf(a.scale) * 1.44269504088896340736f;
     const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
-    hipLaunchKernelGGL(fwd512_kernel, dim3((unsigned)blocks), dim3(G::NT), 0,
+    hipLaunchKernelGGL(fwd512_kernel, dim3((unsigned)((long long)U * BH)), dim3(G::NT), 0,
                        (hipStream_t)a.stream,
                        (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,
-                       (_Float16*)a.o, a.lse, a.B * a.H, a.S, a.causal, c, qsign);
+                       (_Float16*)a.o, a.lse, BH, a.S, a.causal, c, qsign, ch, U, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || U == ch.T) return e;  // no query tile was split
+    const long long merge_blocks = (long long)ch.T * (G::BM / kMergeRows) * BH;
+    hipLaunchKernelGGL(merge512_kernel, dim3((unsigned)merge_blocks), dim3(256), 0,
+                       (hipStream_t)a.stream, ws, (_Float16*)a.o, a.lse, BH, a.S, ch, U);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fused_d512(const FwdArgs& a) { return launch(a); }
+hipError_t launch_fused_d512(const FwdArgs& a) { return launch(a, 0, nullptr); }
+
+size_t splitkv_d512_workspace_floats(int B, int H, int S, int causal, int splits) {
+    const Chunking ch = make_chunking(S, causal, splits);
+    return (size_t)B * H * ch.units() * kSlotFloats;
+}
+
+long long splitkv_d512_units(int S, int causal, int splits) {
+    return make_chunking(S, causal, splits).units();
+}
+
+hipError_t launch_splitkv_d512(const FwdArgs& a, int splits, void* workspace) {
+    return launch(a, splits, (float*)workspace);
+}
 
 }  // namespace attn

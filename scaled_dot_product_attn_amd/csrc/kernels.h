@@ -21,6 +21,14 @@ struct FwdArgs {
 hipError_t launch_fused_pair8_d64_d128(const FwdArgs& a);
 // Fused single-kernel forward, D = 512 (head-dim halves summed in logit space).
 hipError_t launch_fused_d512(const FwdArgs& a);
+// Split-KV forward, D = 512: every query tile's key range cut into chunks of
+// at most ceil(ceil(S/32) / splits) 32-key tiles, partial states in
+// `workspace`, merged by a second kernel.
+hipError_t launch_splitkv_d512(const FwdArgs& a, int splits, void* workspace);
+// Floats of workspace that launch_splitkv_d512 needs, and its number of work
+// units per (batch, head).
+size_t splitkv_d512_workspace_floats(int B, int H, int S, int causal, int splits);
+long long splitkv_d512_units(int S, int causal, int splits);
 // Unfused ablation: QK -> S (fp32, workspace), softmax -> P (fp16, workspace)
 // and LSE, PV -> O.  Three launches on a.stream.
 hipError_t launch_unfused(const FwdArgs& a, void* workspace);

@@ -102,3 +102,43 @@ def test_python_binding_rejects_cpu_tensors(L):
         attn.fwd(q, q, q, causal=True)
     with pytest.raises(TypeError):
         attn.fwd(q.float(), q, q, causal=True)
+
+
+def splitkv_units(S, causal, splits):
+    """Work units (query tile, key chunk) of one (batch, head): 64-row query
+    tiles, 32-key tiles, chunks of at most ceil(ceil(S/32) / splits) tiles."""
+    T = -(-S // 64)
+    C = -(-(-(-S // 32)) // splits)
+    units = 0
+    for qt in range(T):
+        kv_end = min(S, (qt + 1) * 64) if causal else S
+        units += -(-(-(-kv_end // 32)) // C)
+    return units, T
+
+
+@pytest.mark.parametrize("S,causal,splits", [(1024, 1, 4), (1024, 0, 4), (1024, 1, 1),
+                                             (300, 1, 3), (65, 0, 16), (1, 1, 8)])
+def test_splitkv_workspace_bytes(L, S, causal, splits):
+    units, T = splitkv_units(S, causal, splits)
+    slot = (64 * 512 + 2 * 64) * 4
+    expect = 0 if units == T else 2 * 3 * units * slot
+    assert L.attn_fwd_splitkv_workspace_bytes(2, 3, S, 512, causal, splits) == expect
+    if (S, causal, splits) == (1024, 1, 4):
+        assert units == 40  # 1,1,1,1,2,2,2,2,3,3,3,3,4,4,4,4 chunks per query tile
+
+
+def test_splitkv_validation(L):
+    assert L.attn_fwd_splitkv_workspace_bytes(1, 8, 1024, 128, 1, 4) == 0
+    assert L.attn_fwd_splitkv_workspace_bytes(1, 8, 1024, 512, 1, 0) == 0
+    need = L.attn_fwd_splitkv_workspace_bytes(1, 2, 1024, 512, 1, 4)
+    assert need > 0
+    W = 0x90000000
+    args = (Q, K, V, O, LSE, 1, 2, 1024, 512, 1, 0.1)
+    assert L.attn_fwd_splitkv(*args, 4, None, need, None) == C["ATTN_ERR_WORKSPACE"]
+    assert L.attn_fwd_splitkv(*args, 4, W, need - 1, None) == C["ATTN_ERR_WORKSPACE"]
+    assert L.attn_fwd_splitkv(*args, 4, Q, need, None) == C["ATTN_ERR_ALIAS"]
+    assert L.attn_fwd_splitkv(*args, 0, W, need, None) == C["ATTN_ERR_SPLITS"]
+    d128 = (Q, K, V, O, LSE, 1, 2, 1024, 128, 1, 0.1)
+    assert L.attn_fwd_splitkv(*d128, 4, W, need, None) == C["ATTN_ERR_HEAD_DIM"]
+    nul = (None, K, V, O, LSE, 1, 2, 1024, 512, 1, 0.1)
+    assert L.attn_fwd_splitkv(*nul, 4, W, need, None) == C["ATTN_ERR_NULL"]
