@@ -115,7 +115,7 @@ def measured_traffic(workload_name, path):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; the attention forward "
+        print("bench.py: runs on exactly one GPU; the attention forward "
               "shards over (batch, head) slices with no exchange, so a multi-GPU "
               "figure is not measured here.", file=sys.stderr)
         sys.exit(2)
