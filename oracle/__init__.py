@@ -48,11 +48,12 @@ def lib():
         f = ctypes.c_float
         L.oracle_attn_fwd_f64.argtypes = [P, P, P, P, P, i, i, i, i, i, f, i]
         L.oracle_attn_fwd_f64_planted.argtypes = [P, P, P, P, P, i, i, i, i, i, f, i, i]
+        L.oracle_attn_fwd_kv_f64.argtypes = [P, P, P, P, P, i, i, i, i, i, i, f, i, i]
         L.oracle_logits_f64.argtypes = [P, P, P, i, i, i, i, i, i, i, f, i]
         L.oracle_softmax_av_f64.argtypes = [P, P, P, P, i, i, i, i, i]
         L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
         L.oracle_half_to_double.restype = ctypes.c_double
-        for name in ("oracle_attn_fwd_f64", "oracle_attn_fwd_f64_planted",
+        for name in ("oracle_attn_fwd_f64", "oracle_attn_fwd_f64_planted", "oracle_attn_fwd_kv_f64",
                      "oracle_logits_f64", "oracle_softmax_av_f64",
                      "oracle_max_threads"):
             getattr(L, name).restype = ctypes.c_int
@@ -97,6 +98,26 @@ def attn_fwd(q, k, v, causal: bool, scale: float, nthreads: int = 0,
             int(bool(causal)), sc, int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_attn_fwd_f64 failed: {rc}")
+    return o, lse
+
+
+def attn_fwd_kv(q, k, v, causal: bool, scale: float, nthreads: int = 0,
+                planted_mistake: int = 0):
+    """Decode form: q [B,H,Sq,D] against k, v [B,H,Sk,D] -> (O float64
+    [B,H,Sq,D], LSE float64 [B,H,Sq]).  Causal uses bottom-right alignment:
+    key j visible to query i iff j <= i + Sk - Sq."""
+    q, k, v = _f16(q), _f16(k), _f16(v)
+    if k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("q [B,H,Sq,D] and k, v [B,H,Sk,D] do not match")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    o = np.empty((B, H, Sq, D), dtype=np.float64)
+    lse = np.empty((B, H, Sq), dtype=np.float64)
+    rc = lib().oracle_attn_fwd_kv_f64(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq, Sk, D,
+        int(bool(causal)), float(np.float32(scale)), int(nthreads), int(planted_mistake))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attn_fwd_kv_f64 failed: {rc}")
     return o, lse
 
 

@@ -29,15 +29,17 @@ def _exact(x: np.ndarray):
 
 
 def exact_logits(qh, kh, scale: float, causal: bool):
-    """Exact scaled logits for one head: list of rows, None where masked."""
-    S = qh.shape[0]
+    """Exact scaled logits for one head: list of rows, None where masked.
+    With Sq query rows and Sk keys, causal keeps key j for query i iff
+    j <= i + Sk - Sq (bottom-right; j <= i when Sq = Sk)."""
+    Sq, Sk = qh.shape[0], kh.shape[0]
     qe, ke = _exact(qh), _exact(kh)
     sc = Fraction(float(np.float32(scale)))
     out = []
-    for i in range(S):
+    for i in range(Sq):
         row = []
-        for j in range(S):
-            if causal and j > i:
+        for j in range(Sk):
+            if causal and j > i + Sk - Sq:
                 row.append(None)
             else:
                 row.append(sc * sum((a * b for a, b in zip(qe[i], ke[j])), Fraction(0)))
@@ -46,8 +48,10 @@ def exact_logits(qh, kh, scale: float, causal: bool):
 
 
 def attn_fwd(q, k, v, causal: bool, scale: float):
-    """(O, LSE) as float64 arrays for fp16 inputs [B, H, S, D]."""
+    """(O, LSE) as float64 arrays for fp16 inputs q [B, H, Sq, D] and
+    k, v [B, H, Sk, D] (Sq = Sk for the square case)."""
     B, H, S, D = q.shape
+    Sk = k.shape[2]
     o = np.zeros((B, H, S, D), dtype=np.float64)
     lse = np.zeros((B, H, S), dtype=np.float64)
     for b in range(B):
@@ -55,7 +59,7 @@ def attn_fwd(q, k, v, causal: bool, scale: float):
             s = exact_logits(q[b, h], k[b, h], scale, causal)
             vv = v[b, h].astype(np.float64)
             for i in range(S):
-                vis = [j for j in range(S) if s[i][j] is not None]
+                vis = [j for j in range(Sk) if s[i][j] is not None]
                 m = max(s[i][j] for j in vis)
                 p = {j: math.exp(float(s[i][j] - m)) for j in vis}
                 l = math.fsum(p.values())

@@ -24,6 +24,15 @@
  * exact fp16 values widened to double and the scale is the float32 value the
  * GPU receives, widened exactly.
  *
+ * Decode (query length Sq different from key length Sk, a few queries against
+ * a long key/value cache; the decode kernel of "Validating Memory-Optimal
+ * Transformer Kernels on Real Hardware", section 5): the same definition with
+ * q, o of shape [B, H, Sq, D] and k, v of shape [B, H, Sk, D].  The pages fix
+ * no alignment for the causal mask when Sq != Sk; the reading taken here is
+ * bottom-right alignment, the one a cache of past keys implies: query i is the
+ * (Sk - Sq + i)-th position, so key j is visible iff j <= i + (Sk - Sq).  With
+ * Sq = Sk this is the j <= i rule above.
+ *
  * Engineering: build with -O2 -ffp-contract=off and no fast-math, so every sum
  * is evaluated in the written order.  Rows are independent; OpenMP splits over
  * rows only, so results do not depend on the thread count.  Per-row scratch is
@@ -92,24 +101,31 @@ int oracle_max_threads(void)
  *   4: O not divided by l
  *   5: key and query roles swapped in the dot product (q[j] . k[i])
  *   6: last head-dim element dropped from the dot product
+ *   7: causal mask aligned top-left (key j visible iff j <= i) when Sq != Sk
  */
-static int visible(int causal, int mistake, int i, int j)
+static int visible(int causal, int mistake, int i, int j, int off)
 {
     if (!causal)
         return 1;
     if (mistake == 1)
-        return j < i + 2;
-    return j <= i;
+        return j < i + off + 2;
+    if (mistake == 7)
+        return j <= i;
+    return j <= i + off;
 }
 
+/* Sq query rows against Sk keys; off = Sk - Sq is the causal alignment. */
 static int run(const uint16_t *q16, const uint16_t *k16, const uint16_t *v16,
-               double *o, double *lse, int B, int H, int S, int D, int causal,
+               double *o, double *lse, int B, int H, int Sq, int Sk, int D, int causal,
                float scale, int nthreads, int mistake)
 {
-    if (B < 1 || H < 1 || S < 1 || D < 1)
+    if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1)
         return -1;
-    size_t n = (size_t)B * H * S * D;
-    double *q = widen(q16, n), *k = widen(k16, n), *v = widen(v16, n);
+    if (causal && Sq > Sk)
+        return -3; /* the first Sq - Sk rows would see no key */
+    const int off = Sk - Sq;
+    size_t nq = (size_t)B * H * Sq * D, nk = (size_t)B * H * Sk * D;
+    double *q = widen(q16, nq), *k = widen(k16, nk), *v = widen(v16, nk);
     if (!q || !k || !v) {
         free(q);
         free(k);
@@ -118,12 +134,12 @@ static int run(const uint16_t *q16, const uint16_t *k16, const uint16_t *v16,
     }
     const double sc = (mistake == 2) ? 1.0 : (double)scale;
     const int dlen = (mistake == 6 && D > 1) ? D - 1 : D;
-    const long rows = (long)B * H * S;
+    const long rows = (long)B * H * Sq;
     int err = 0;
     set_threads(nthreads);
 #pragma omp parallel
     {
-        double *s = (double *)malloc((size_t)S * sizeof(double));
+        double *s = (double *)malloc((size_t)Sk * sizeof(double));
         double *acc = (double *)malloc((size_t)D * sizeof(double));
         if (!s || !acc) {
 #pragma omp atomic write
@@ -131,15 +147,15 @@ static int run(const uint16_t *q16, const uint16_t *k16, const uint16_t *v16,
         } else {
 #pragma omp for schedule(static)
             for (long r = 0; r < rows; ++r) {
-                const long bh = r / S;
-                const int i = (int)(r % S);
-                const double *Q = q + (size_t)bh * S * D;
-                const double *K = k + (size_t)bh * S * D;
-                const double *V = v + (size_t)bh * S * D;
+                const long bh = r / Sq;
+                const int i = (int)(r % Sq);
+                const double *Q = q + (size_t)bh * Sq * D;
+                const double *K = k + (size_t)bh * Sk * D;
+                const double *V = v + (size_t)bh * Sk * D;
                 /* logits over visible keys; -inf marks a masked key */
                 double m = -INFINITY;
-                for (int j = 0; j < S; ++j) {
-                    if (!visible(causal, mistake, i, j)) {
+                for (int j = 0; j < Sk; ++j) {
+                    if (!visible(causal, mistake, i, j, off)) {
                         s[j] = -INFINITY;
                         continue;
                     }
@@ -154,14 +170,14 @@ static int run(const uint16_t *q16, const uint16_t *k16, const uint16_t *v16,
                 }
                 /* weights and their sum, keys ascending */
                 double l = 0.0;
-                for (int j = 0; j < S; ++j) {
+                for (int j = 0; j < Sk; ++j) {
                     s[j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m);
                     l += s[j];
                 }
                 for (int d = 0; d < D; ++d)
                     acc[d] = 0.0;
-                for (int j = 0; j < S; ++j) {
-                    if (!visible(causal, mistake, i, j))
+                for (int j = 0; j < Sk; ++j) {
+                    if (!visible(causal, mistake, i, j, off))
                         continue; /* weight exactly 0 */
                     const double *vj = V + (size_t)j * D;
                     for (int d = 0; d < D; ++d)
@@ -193,7 +209,7 @@ int oracle_attn_fwd_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         double *o, double *lse, int B, int H, int S, int D,
                         int causal, float scale, int nthreads)
 {
-    return run(q, k, v, o, lse, B, H, S, D, causal, scale, nthreads, 0);
+    return run(q, k, v, o, lse, B, H, S, S, D, causal, scale, nthreads, 0);
 }
 
 /* The same computation with one planted mistake (see the list above). */
@@ -202,7 +218,19 @@ int oracle_attn_fwd_f64_planted(const uint16_t *q, const uint16_t *k,
                                 int B, int H, int S, int D, int causal,
                                 float scale, int nthreads, int mistake)
 {
-    return run(q, k, v, o, lse, B, H, S, D, causal, scale, nthreads, mistake);
+    return run(q, k, v, o, lse, B, H, S, S, D, causal, scale, nthreads, mistake);
+}
+
+/*
+ * Decode form: q, o [B, H, Sq, D]; k, v [B, H, Sk, D]; lse [B, H, Sq].
+ * Causal: key j visible to query i iff j <= i + (Sk - Sq) (bottom-right);
+ * returns -3 when causal and Sq > Sk.  `mistake` as above (0 = as specified).
+ */
+int oracle_attn_fwd_kv_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           double *o, double *lse, int B, int H, int Sq, int Sk, int D,
+                           int causal, float scale, int nthreads, int mistake)
+{
+    return run(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, nthreads, mistake);
 }
 
 /*
