@@ -52,7 +52,9 @@ def parse():
                    help="1..5 (default 3: B=1 H=32 S=1024 D=128 causal)")
     p.add_argument("--rotate", type=int, default=1,
                    help="cycle through this many independent input sets")
-    p.add_argument("--path", choices=["fused", "unfused", "splitkv"], default="fused")
+    p.add_argument("--path", choices=["fused", "unfused", "splitkv", "decode"], default="fused")
+    p.add_argument("--decode", type=int, default=1,
+                   help="decode path: 1..3, the decode workload (Sq rows against Sk keys)")
     p.add_argument("--splits", type=int, default=3,
                    help="split-KV path: chunks of the longest key range (D = 512 only)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -133,25 +135,34 @@ def main():
     import scaled_dot_product_attn_amd as attn
     from scaled_dot_product_attn_amd import inputs
 
-    w = inputs.WORKLOADS[args.workload]
+    decode = args.path == "decode"
+    w = inputs.DECODE_WORKLOADS[args.decode] if decode else inputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     attn.load_library()
     sets = []
     for r in range(args.rotate):
         if r == 0:
             q, k, v = w.qkv()
+        elif decode:
+            q, k, v = inputs.DecodeWorkload(w.name, w.B, w.H, w.Sq, w.Sk, w.D, w.causal,
+                                            w.seed_base + 100 * r).qkv()
         else:
             q, k, v = (inputs.normal_f16(w.seed_base + 100 * r + t, w.shape, w.sigma)
                        for t in range(3))
         sets.append(tuple(torch.from_numpy(x).to(dev) for x in (q, k, v)))
-    o = torch.empty(w.shape, dtype=torch.float16, device=dev)
-    lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
+    qshape = (w.B, w.H, w.Sq, w.D) if decode else w.shape
+    o = torch.empty(qshape, dtype=torch.float16, device=dev)
+    lse = torch.empty(qshape[:3], dtype=torch.float32, device=dev)
     ws = None
     if args.path == "unfused":
         ws = torch.empty(attn.unfused_workspace_bytes(w.B, w.H, w.S), dtype=torch.uint8,
                          device=dev)
     elif args.path == "splitkv":
         nbytes = attn.splitkv_workspace_bytes(w.B, w.H, w.S, w.D, w.causal, args.splits)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    elif decode:
+        dsplits = attn.decode_splits(w.B, w.H, w.Sq, w.Sk)
+        nbytes = attn.decode_workspace_bytes(w.B, w.H, w.Sq, w.Sk, w.D, w.causal, dsplits)
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
 
     def step(i):
@@ -161,9 +172,12 @@ def main():
         elif args.path == "unfused":
             attn.fwd_unfused(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse,
                              workspace=ws)
-        else:
+        elif args.path == "splitkv":
             attn.fwd_splitkv(q, k, v, causal=w.causal, scale=w.scale, splits=args.splits,
                              out=o, lse=lse, workspace=ws)
+        else:
+            attn.fwd_decode(q, k, v, causal=w.causal, scale=w.scale, splits=dsplits,
+                            out=o, lse=lse, workspace=ws)
 
     stream = torch.cuda.current_stream(dev)  # the stream attn.fwd launches on
     for i in range(args.warmup):
@@ -200,7 +214,8 @@ def main():
     flops, nbytes = w.flops(), w.alg_bytes()
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (mean_us * 1e-6) / 1e12
-    bound_mfma = w.D >= 128 and w.causal  # the D=128/512 causal shapes sit near the ridge
+    # the square D=128/512 causal shapes sit near the ridge; decode streams K/V
+    bound_mfma = not decode and w.D >= 128 and w.causal
     if bound_mfma:
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_FP16_TFLOPS, "traffic": None}
@@ -225,8 +240,10 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16 (fp32 accumulate)",
         "data": "synthetic (seeded SplitMix64/Box-Muller normals, fp16 RNE)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
-                   "causal": w.causal, "scale": w.scale, "sigma": w.sigma,
+        "config": {"workload": w.name, "B": w.B, "H": w.H,
+                   **({"Sq": w.Sq, "Sk": w.Sk, "splits": dsplits} if decode else {"S": w.S}),
+                   "D": w.D,
+                   "causal": w.causal, "scale": w.scale, "sigma": getattr(w, "sigma", 1.0),
                    "path": args.path, "input_sets": args.rotate,
                    **({"splits": args.splits} if args.path == "splitkv" else {}),
                    "cache": "warm (same buffers)" if args.rotate == 1 else
@@ -239,7 +256,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not decode:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

@@ -128,6 +128,34 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                      int B, int H, int S, int D, int causal, float scale, int splits,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode form: Sq query rows against Sk keys, e.g. a few new tokens against a
+ * long key/value cache (the decode kernel of "Validating Memory-Optimal
+ * Transformer Kernels on Real Hardware", section 5).
+ *   q, o : device fp16 [B, H, Sq, D]       k, v : device fp16 [B, H, Sk, D]
+ *   lse  : device fp32 [B, H, Sq]
+ *   D    : 64 or 128 (else ATTN_ERR_HEAD_DIM)
+ *   causal != 0 aligns the mask bottom-right: query i is position
+ *     i + Sk - Sq of the sequence, so key j is visible iff j <= i + Sk - Sq
+ *     (with Sq = Sk this is attn_fwd's mask).  It needs Sq <= Sk, else
+ *     ATTN_ERR_SHAPE (the first rows would see no key).
+ *   splits : >= 1 (else ATTN_ERR_SPLITS).  The key range of every 64-row
+ *     query tile is cut into chunks of at most ceil(ceil(Sk/64) / splits)
+ *     64-key tiles, one workgroup each; chunks leave partial states in
+ *     `workspace` and a second kernel merges them in chunk order
+ *     (deterministic; exact up to rounding because the key sets are
+ *     disjoint).  Query tiles with one chunk are written directly.
+ *   workspace : device memory of at least attn_fwd_decode_workspace_bytes(...)
+ *     bytes, owned by the caller and overwritten; may be NULL when that size
+ *     is 0.
+ * One or two launches on `stream`, asynchronous like attn_fwd.
+ */
+size_t attn_fwd_decode_workspace_bytes(int B, int H, int Sq, int Sk, int D, int causal,
+                                       int splits);
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Sq, int Sk, int D, int causal, float scale, int splits,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* 1 if attn_fwd accepts head dimension D, else 0. */
 int attn_head_dim_supported(int D);
 

@@ -14,12 +14,13 @@ import os
 from .build import LIB_PATH
 
 __all__ = ["AttnError", "fwd", "fwd_unfused", "unfused_workspace_bytes", "fwd_splitkv",
-           "splitkv_workspace_bytes", "head_dim_supported", "load_library", "LIB_PATH",
+           "splitkv_workspace_bytes", "fwd_decode", "decode_workspace_bytes", "decode_splits", "head_dim_supported", "load_library", "LIB_PATH",
            "SYMBOLS"]
 
 # Every symbol include/attn.h declares.
 SYMBOLS = ("attn_fwd", "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
            "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
+           "attn_fwd_decode", "attn_fwd_decode_workspace_bytes",
            "attn_head_dim_supported", "attn_status_string", "attn_last_hip_error")
 
 ATTN_ERR_LAUNCH = -5
@@ -62,6 +63,10 @@ def load_library(path: str = LIB_PATH):
     L.attn_fwd_splitkv.restype = I
     L.attn_fwd_splitkv_workspace_bytes.argtypes = [I, I, I, I, I, I]
     L.attn_fwd_splitkv_workspace_bytes.restype = Z
+    L.attn_fwd_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
+    L.attn_fwd_decode.restype = I
+    L.attn_fwd_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    L.attn_fwd_decode_workspace_bytes.restype = Z
     L.attn_head_dim_supported.argtypes = [I]
     L.attn_head_dim_supported.restype = I
     L.attn_status_string.argtypes = [I]
@@ -174,4 +179,60 @@ def fwd_splitkv(q, k, v, *, causal: bool, splits: int = 4, scale: float | None =
     _check(L.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                               lse.data_ptr(), B, H, S, D, int(bool(causal)), scale, int(splits),
                               wptr, wbytes, stream))
+    return out, lse
+
+
+def decode_workspace_bytes(B: int, H: int, Sq: int, Sk: int, D: int, causal: bool,
+                           splits: int) -> int:
+    return int(load_library().attn_fwd_decode_workspace_bytes(B, H, Sq, Sk, D,
+                                                               int(bool(causal)), splits))
+
+
+def decode_splits(B: int, H: int, Sq: int, Sk: int, target_units: int = 512) -> int:
+    """A default chunk count: enough (batch, head, query tile, chunk) units to
+    give every CU of an MI355X (256) about two workgroups, and at most one
+    chunk per 64-key tile."""
+    tiles = -(-Sq // 64)
+    return max(1, min(-(-Sk // 64), -(-target_units // (B * H * tiles))))
+
+
+def fwd_decode(q, k, v, *, causal: bool, splits: int | None = None,
+               scale: float | None = None, out=None, lse=None, workspace=None):
+    """Decode form: q [B, H, Sq, D] against k, v [B, H, Sk, D] (contiguous fp16
+    on the GPU, D = 64 or 128); causal aligned bottom-right.  Returns
+    (o fp16 [B, H, Sq, D], lse fp32 [B, H, Sq])."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.float16:
+            raise TypeError(f"{name} must be float16, got {t.dtype}")
+        if t.device.type != "cuda" or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != H or k.shape[3] != D:
+        raise ValueError(f"k, v must be [B, H, Sk, D] matching q: {q.shape} {k.shape} {v.shape}")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.float16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float16 tensor shaped like q")
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, Sq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if splits is None:
+        splits = decode_splits(B, H, Sq, Sk)
+    L = load_library()
+    need = decode_workspace_bytes(B, H, Sq, Sk, D, causal, splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(L.attn_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), B, H, Sq, Sk, D, int(bool(causal)), float(scale),
+                             int(splits), wptr, wbytes, stream))
     return out, lse

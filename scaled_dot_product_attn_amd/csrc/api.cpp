@@ -112,6 +112,46 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
     return launched(attn::launch_splitkv_d512(a, splits, need > 0 ? workspace : nullptr));
 }
 
+size_t attn_fwd_decode_workspace_bytes(int B, int H, int Sq, int Sk, int D, int causal,
+                                       int splits) {
+    if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || (D != 64 && D != 128) || splits < 1) return 0;
+    return attn::decode_workspace_floats(B, H, Sq, Sk, D, causal != 0, splits) * sizeof(float);
+}
+
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Sq, int Sk, int D, int causal, float scale, int splits,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+    if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1) return ATTN_ERR_SHAPE;
+    const long long bh = (long long)B * H;
+    if (bh > INT32_MAX || bh * Sq > INT32_MAX / 2 || bh * Sk > INT32_MAX / 2 ||
+        (causal && Sq > Sk))
+        return ATTN_ERR_SHAPE;
+    if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+    if (!isfinite(scale)) return ATTN_ERR_SCALE;
+    if (splits < 1) return ATTN_ERR_SPLITS;
+    if (bh * attn::decode_units(Sq, Sk, causal != 0, splits) > INT32_MAX ||
+        bh * ((Sq + 63) / 64) * 8 > INT32_MAX)
+        return ATTN_ERR_SHAPE;
+    const size_t nq = (size_t)bh * Sq * D * 2, nk = (size_t)bh * Sk * D * 2,
+                 nl = (size_t)bh * Sq * 4;
+    if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nk) || overlaps(o, nq, v, nk) ||
+        overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nk) ||
+        overlaps(lse, nl, o, nq))
+        return ATTN_ERR_ALIAS;
+    const size_t need = attn_fwd_decode_workspace_bytes(B, H, Sq, Sk, D, causal, splits);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+        if (overlaps(workspace, need, q, nq) || overlaps(workspace, need, k, nk) ||
+            overlaps(workspace, need, v, nk) || overlaps(workspace, need, o, nq) ||
+            overlaps(workspace, need, lse, nl))
+            return ATTN_ERR_ALIAS;
+    }
+    const attn::DecArgs a{q, k, v, o, lse, B, H, Sq, Sk, D, causal != 0, scale, splits,
+                          need > 0 ? workspace : nullptr, stream};
+    return launched(attn::launch_decode(a));
+}
+
 const char* attn_status_string(int status) {
     switch (status) {
         case ATTN_OK: return "ok";

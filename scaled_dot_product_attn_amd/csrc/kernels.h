@@ -29,6 +29,27 @@ hipError_t launch_splitkv_d512(const FwdArgs& a, int splits, void* workspace);
 // units per (batch, head).
 size_t splitkv_d512_workspace_floats(int B, int H, int S, int causal, int splits);
 long long splitkv_d512_units(int S, int causal, int splits);
+// Decode form: Sq query rows against Sk keys (causal aligned bottom-right),
+// D = 64 or 128, key ranges in chunks of at most ceil(ceil(Sk/64) / splits)
+// 64-key tiles, partial states in `workspace` merged by a second kernel.
+struct DecArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, H, Sq, Sk, D;
+    int causal;
+    float scale;
+    int splits;
+    void* workspace;
+    void* stream;
+};
+hipError_t launch_decode(const DecArgs& a);
+// Work units per (batch, head) and workspace floats (0 when no query tile is
+// split) of launch_decode.
+long long decode_units(int Sq, int Sk, int causal, int splits);
+size_t decode_workspace_floats(int B, int H, int Sq, int Sk, int D, int causal, int splits);
 // Unfused ablation: QK -> S (fp32, workspace), softmax -> P (fp16, workspace)
 // and LSE, PV -> O.  Three launches on a.stream.
 hipError_t launch_unfused(const FwdArgs& a, void* workspace);

@@ -123,3 +123,55 @@ WORKLOADS = {
     4: Workload("B8_H32_S512_D128_causal", 8, 32, 512, 128, True, 1.0, 4000),
     5: Workload("B1_H8_S1024_D512_causal", 1, 8, 1024, 512, True, 0.5, 5000),
 }
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Sq query rows against Sk keys: q [B, H, Sq, D], k and v [B, H, Sk, D]."""
+
+    name: str
+    B: int
+    H: int
+    Sq: int
+    Sk: int
+    D: int
+    causal: bool
+    seed_base: int
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / np.sqrt(self.D)))
+
+    def visible_pairs(self) -> int:
+        """(query, key) pairs inside the mask (bottom-right when causal)."""
+        if not self.causal:
+            return self.Sq * self.Sk
+        off = self.Sk - self.Sq
+        return sum(min(self.Sk, i + off + 1) for i in range(self.Sq))
+
+    def flops(self) -> float:
+        """Effective FLOPs: 4 B H D per visible (query, key) pair."""
+        return 4.0 * self.B * self.H * self.D * self.visible_pairs()
+
+    def alg_bytes(self) -> int:
+        """Read Q, K, V once, write O (fp16) and the fp32 log-sum-exp."""
+        bh = self.B * self.H
+        return 2 * bh * self.D * (2 * self.Sq + 2 * self.Sk) + 4 * bh * self.Sq
+
+    def qkv(self):
+        """(q, k, v) as fp16 numpy arrays; seeds seed_base + 0, 1, 2."""
+        return (normal_f16(self.seed_base, (self.B, self.H, self.Sq, self.D)),
+                normal_f16(self.seed_base + 1, (self.B, self.H, self.Sk, self.D)),
+                normal_f16(self.seed_base + 2, (self.B, self.H, self.Sk, self.D)))
+
+
+# Decode shapes (a single or a few new rows against a long key/value cache, the
+# O(n) decode kernel whose cost "Validating Memory-Optimal Transformer Kernels
+# on Real Hardware" measures against cache length in section 5).  The pages
+# give no head or batch counts for it; these reuse the case table's
+# H = 32, D = 128.  Seeds are 1000*(10+c) + {0, 1, 2}.
+DECODE_WORKLOADS = {
+    1: DecodeWorkload("decode_B1_H32_Sq1_Sk4096_D128", 1, 32, 1, 4096, 128, True, 11000),
+    2: DecodeWorkload("decode_B1_H32_Sq1_Sk65536_D128", 1, 32, 1, 65536, 128, True, 12000),
+    3: DecodeWorkload("decode_B8_H32_Sq4_Sk8192_D128", 8, 32, 4, 8192, 128, True, 13000),
+}

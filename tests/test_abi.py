@@ -142,3 +142,47 @@ def test_splitkv_validation(L):
     assert L.attn_fwd_splitkv(*d128, 4, W, need, None) == C["ATTN_ERR_HEAD_DIM"]
     nul = (None, K, V, O, LSE, 1, 2, 1024, 512, 1, 0.1)
     assert L.attn_fwd_splitkv(*nul, 4, W, need, None) == C["ATTN_ERR_NULL"]
+
+
+def decode_units(Sq, Sk, causal, splits):
+    """Work units of one (batch, head) in the decode form: 64-row query tiles,
+    64-key tiles, chunks of at most ceil(ceil(Sk/64) / splits) tiles, each
+    tile's key range ending at its last row's visible key (bottom-right)."""
+    Tq = -(-Sq // 64)
+    C = -(-(-(-Sk // 64)) // splits)
+    units = 0
+    for qt in range(Tq):
+        kv_end = min(Sk, min(Sq, (qt + 1) * 64) - 1 + (Sk - Sq) + 1) if causal else Sk
+        units += -(-(-(-kv_end // 64)) // C)
+    return units, Tq
+
+
+@pytest.mark.parametrize("Sq,Sk,D,causal,splits", [(1, 4096, 128, 1, 8), (4, 8192, 64, 0, 3),
+                                                   (130, 2000, 128, 1, 5), (64, 64, 64, 1, 1),
+                                                   (200, 200, 128, 1, 4)])
+def test_decode_workspace_bytes(L, Sq, Sk, D, causal, splits):
+    units, Tq = decode_units(Sq, Sk, causal, splits)
+    expect = 0 if units == Tq else 2 * 3 * units * (64 * D + 128) * 4
+    assert L.attn_fwd_decode_workspace_bytes(2, 3, Sq, Sk, D, causal, splits) == expect
+
+
+def test_decode_validation(L):
+    need = L.attn_fwd_decode_workspace_bytes(1, 2, 1, 4096, 128, 1, 8)
+    assert need == 1 * 2 * 8 * (64 * 128 + 128) * 4
+    W = 0x90000000
+    def dec(q=Q, k=K, v=V, o=O, lse=LSE, B=1, H=2, Sq=1, Sk=4096, D=128, causal=1,
+            scale=0.1, splits=8, ws=W, wb=need):
+        return L.attn_fwd_decode(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, splits,
+                                 ws, wb, None)
+    assert dec(ws=None) == C["ATTN_ERR_WORKSPACE"]
+    assert dec(wb=need - 1) == C["ATTN_ERR_WORKSPACE"]
+    assert dec(ws=Q) == C["ATTN_ERR_ALIAS"]
+    assert dec(splits=0) == C["ATTN_ERR_SPLITS"]
+    assert dec(D=512) == C["ATTN_ERR_HEAD_DIM"]
+    assert dec(Sq=5, Sk=4) == C["ATTN_ERR_SHAPE"]        # causal needs Sq <= Sk
+    assert dec(Sk=0) == C["ATTN_ERR_SHAPE"]
+    assert dec(q=None) == C["ATTN_ERR_NULL"]
+    assert dec(scale=math.nan) == C["ATTN_ERR_SCALE"]
+    assert dec(lse=O) == C["ATTN_ERR_ALIAS"]
+    # one chunk per query tile needs no workspace
+    assert L.attn_fwd_decode_workspace_bytes(1, 2, 1, 4096, 128, 1, 1) == 0
