@@ -49,11 +49,13 @@ def lib():
         L.oracle_attn_fwd_f64.argtypes = [P, P, P, P, P, i, i, i, i, i, f, i]
         L.oracle_attn_fwd_f64_planted.argtypes = [P, P, P, P, P, i, i, i, i, i, f, i, i]
         L.oracle_attn_fwd_kv_f64.argtypes = [P, P, P, P, P, i, i, i, i, i, i, f, i, i]
+        L.oracle_attn_bwd_f64.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, f, i, i]
         L.oracle_logits_f64.argtypes = [P, P, P, i, i, i, i, i, i, i, f, i]
         L.oracle_softmax_av_f64.argtypes = [P, P, P, P, i, i, i, i, i]
         L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
         L.oracle_half_to_double.restype = ctypes.c_double
         for name in ("oracle_attn_fwd_f64", "oracle_attn_fwd_f64_planted", "oracle_attn_fwd_kv_f64",
+                     "oracle_attn_bwd_f64",
                      "oracle_logits_f64", "oracle_softmax_av_f64",
                      "oracle_max_threads"):
             getattr(L, name).restype = ctypes.c_int
@@ -119,6 +121,23 @@ def attn_fwd_kv(q, k, v, causal: bool, scale: float, nthreads: int = 0,
     if rc != 0:
         raise RuntimeError(f"oracle_attn_fwd_kv_f64 failed: {rc}")
     return o, lse
+
+
+def attn_bwd(q, k, v, do, causal: bool, scale: float, nthreads: int = 0,
+             planted_mistake: int = 0):
+    """Gradients (dQ, dK, dV), float64 [B,H,S,D], of sum(dO * O) for the
+    forward softmax(scale Q K^T + mask) V; inputs fp16 [B,H,S,D]."""
+    q, k, v, do = _f16(q), _f16(k), _f16(v), _f16(do)
+    if not (q.shape == k.shape == v.shape == do.shape):
+        raise ValueError("q, k, v, do shapes differ")
+    B, H, S, D = q.shape
+    dq, dk, dv = (np.empty((B, H, S, D), dtype=np.float64) for _ in range(3))
+    rc = lib().oracle_attn_bwd_f64(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, H, S, D,
+        int(bool(causal)), float(np.float32(scale)), int(nthreads), int(planted_mistake))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attn_bwd_f64 failed: {rc}")
+    return dq, dk, dv
 
 
 def logits(q, k, causal: bool, scale: float, d0: int = 0, d1: int | None = None,

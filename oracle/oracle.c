@@ -333,3 +333,116 @@ int oracle_softmax_av_f64(const double *logits, const uint16_t *v16, double *o,
     free(v);
     return err;
 }
+
+/*
+ * Backward pass of the forward above, in float64, for L = sum(dO * O):
+ *   P[i,j]  = softmax_j(scale q_i.k_j + mask)        (the forward's weights)
+ *   dV[j]   = sum_i P[i,j] dO[i]
+ *   dP[i,j] = dO[i] . v[j]
+ *   Dlt[i]  = dO[i] . O[i]          (= sum_j P[i,j] dP[i,j])
+ *   dS[i,j] = P[i,j] (dP[i,j] - Dlt[i])
+ *   dQ[i]   = scale sum_j dS[i,j] k[j],   dK[j] = scale sum_i dS[i,j] q[i]
+ * The step after the forward ("Validating Memory-Optimal Transformer Kernels
+ * on Real Hardware", sections 1.2 and 4: the backward kernel and the fused
+ * forward+backward that avoid the O(n^2) intermediate); the chain rule of the
+ * softmax is the plain one.  q, k, v, dO: fp16 bits [B, H, S, D];
+ * dq, dk, dv: float64 [B, H, S, D], overwritten.  Sums run in index order;
+ * heads are independent and OpenMP splits over heads only.
+ * `mistake` (0 = as specified) plants one error for the pins' power tests:
+ *   1: Dlt dropped (dS = P dP)   2: scale dropped from dQ and dK
+ *   3: dV from unnormalised weights   4: causal mask off by one
+ */
+int oracle_attn_bwd_f64(const uint16_t *q16, const uint16_t *k16, const uint16_t *v16,
+                        const uint16_t *do16, double *dq, double *dk, double *dv,
+                        int B, int H, int S, int D, int causal, float scale, int nthreads,
+                        int mistake)
+{
+    if (B < 1 || H < 1 || S < 1 || D < 1)
+        return -1;
+    size_t n = (size_t)B * H * S * D;
+    double *q = widen(q16, n), *k = widen(k16, n), *v = widen(v16, n), *g = widen(do16, n);
+    if (!q || !k || !v || !g) {
+        free(q);
+        free(k);
+        free(v);
+        free(g);
+        return -2;
+    }
+    const double sc = (double)scale;
+    const long heads = (long)B * H;
+    int err = 0;
+    memset(dk, 0, n * sizeof(double));
+    memset(dv, 0, n * sizeof(double));
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double *p = (double *)malloc((size_t)S * sizeof(double));
+        double *dp = (double *)malloc((size_t)S * sizeof(double));
+        double *o = (double *)malloc((size_t)D * sizeof(double));
+        if (!p || !dp || !o) {
+#pragma omp atomic write
+            err = -2;
+        } else {
+#pragma omp for schedule(static)
+            for (long bh = 0; bh < heads; ++bh) {
+                const double *Q = q + (size_t)bh * S * D, *K = k + (size_t)bh * S * D;
+                const double *V = v + (size_t)bh * S * D, *G = g + (size_t)bh * S * D;
+                double *dQ = dq + (size_t)bh * S * D, *dK = dk + (size_t)bh * S * D;
+                double *dV = dv + (size_t)bh * S * D;
+                for (int i = 0; i < S; ++i) {
+                    const int last = !causal ? S - 1 : (mistake == 4 ? (i + 1 < S ? i + 1 : S - 1) : i);
+                    double m = -INFINITY;
+                    for (int j = 0; j <= last; ++j) {
+                        double dot = 0.0;
+                        for (int d = 0; d < D; ++d)
+                            dot += Q[(size_t)i * D + d] * K[(size_t)j * D + d];
+                        p[j] = sc * dot;
+                        if (p[j] > m)
+                            m = p[j];
+                    }
+                    double l = 0.0;
+                    for (int j = 0; j <= last; ++j) {
+                        p[j] = exp(p[j] - m);
+                        l += p[j];
+                    }
+                    /* O[i] and Dlt[i] */
+                    for (int d = 0; d < D; ++d)
+                        o[d] = 0.0;
+                    for (int j = 0; j <= last; ++j)
+                        for (int d = 0; d < D; ++d)
+                            o[d] += p[j] * V[(size_t)j * D + d];
+                    double dlt = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        dlt += G[(size_t)i * D + d] * (o[d] / l);
+                    for (int j = 0; j <= last; ++j) {
+                        double t = 0.0;
+                        for (int d = 0; d < D; ++d)
+                            t += G[(size_t)i * D + d] * V[(size_t)j * D + d];
+                        dp[j] = t;
+                    }
+                    for (int d = 0; d < D; ++d)
+                        dQ[(size_t)i * D + d] = 0.0;
+                    const double gs = (mistake == 2) ? 1.0 : sc;
+                    for (int j = 0; j <= last; ++j) {
+                        const double pn = p[j] / l;
+                        const double ds = (mistake == 1) ? pn * dp[j] : pn * (dp[j] - dlt);
+                        const double pv = (mistake == 3) ? p[j] : pn;
+                        for (int d = 0; d < D; ++d) {
+                            dQ[(size_t)i * D + d] += gs * ds * K[(size_t)j * D + d];
+                            dK[(size_t)j * D + d] += gs * ds * Q[(size_t)i * D + d];
+                            dV[(size_t)j * D + d] += pv * G[(size_t)i * D + d];
+                        }
+                    }
+                }
+            }
+        }
+        free(p);
+        free(dp);
+        free(o);
+    }
+    free(q);
+    free(k);
+    free(v);
+    free(g);
+    return err;
+}
