@@ -52,7 +52,8 @@ def parse():
                    help="1..5 (default 3: B=1 H=32 S=1024 D=128 causal)")
     p.add_argument("--rotate", type=int, default=1,
                    help="cycle through this many independent input sets")
-    p.add_argument("--path", choices=["fused", "unfused", "splitkv", "decode"], default="fused")
+    p.add_argument("--path", choices=["fused", "unfused", "splitkv", "decode", "bwd"],
+                   default="fused")
     p.add_argument("--decode", type=int, default=1,
                    help="decode path: 1..3, the decode workload (Sq rows against Sk keys)")
     p.add_argument("--splits", type=int, default=3,
@@ -64,6 +65,32 @@ def parse():
                    help="only run a plain device copy of this many MiB (the reference "
                         "kernel for scaling HBM byte counters) and exit")
     return p.parse_args()
+
+
+def cpu_baseline_bwd(w, min_seconds):
+    """The float64 oracle's backward on this host's cores, over the first
+    heads of the workload (as many as fit about min_seconds), scaled to the
+    algorithmic FLOPs of those heads."""
+    import oracle
+    from scaled_dot_product_attn_amd import inputs
+    oracle.build(force=False)
+    q, k, v = w.qkv()
+    do = inputs.normal_f16(w.seed_base + 50, w.shape, 1.0)
+    threads = oracle.max_threads()
+    h = 1
+    while True:
+        sl = (slice(0, 1), slice(0, h))
+        t0 = time.perf_counter()
+        oracle.attn_bwd(q[sl], k[sl], v[sl], do[sl], w.causal, w.scale, nthreads=threads)
+        sec = time.perf_counter() - t0
+        if sec >= min_seconds or h >= w.H:
+            break
+        h = min(w.H, h * 2)
+    flops = 2.5 * w.flops() * h / (w.B * w.H)
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds_per_call": sec,
+            "sample": f"{h} of the {w.B * w.H} heads of {w.name} (float64 C oracle backward, "
+                      f"OpenMP over heads), one call"}
 
 
 def cpu_baseline(w, min_seconds):
@@ -164,6 +191,17 @@ def main():
         dsplits = attn.decode_splits(w.B, w.H, w.Sq, w.Sk)
         nbytes = attn.decode_workspace_bytes(w.B, w.H, w.Sq, w.Sk, w.D, w.causal, dsplits)
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    elif args.path == "bwd":
+        # the forward's O and LSE of every input set, and dO drawn like Q
+        fw = []
+        for r, (q, k, v) in enumerate(sets):
+            of, lf = attn.fwd(q, k, v, causal=w.causal, scale=w.scale)
+            do = torch.from_numpy(inputs.normal_f16(w.seed_base + 50 + 100 * r, w.shape,
+                                                    1.0)).to(dev)
+            fw.append((of, lf, do))
+        grads = tuple(torch.empty(w.shape, dtype=torch.float16, device=dev) for _ in range(3))
+        ws = torch.empty(attn.bwd_workspace_bytes(w.B, w.H, w.S), dtype=torch.uint8,
+                         device=dev)
 
     def step(i):
         q, k, v = sets[i % len(sets)]
@@ -175,6 +213,10 @@ def main():
         elif args.path == "splitkv":
             attn.fwd_splitkv(q, k, v, causal=w.causal, scale=w.scale, splits=args.splits,
                              out=o, lse=lse, workspace=ws)
+        elif args.path == "bwd":
+            of, lf, do = fw[i % len(sets)]
+            attn.bwd(q, k, v, of, lf, do, causal=w.causal, scale=w.scale, dq=grads[0],
+                     dk=grads[1], dv=grads[2], workspace=ws)
         else:
             attn.fwd_decode(q, k, v, causal=w.causal, scale=w.scale, splits=dsplits,
                             out=o, lse=lse, workspace=ws)
@@ -212,6 +254,12 @@ def main():
     p90 = per_us[int(0.9 * (len(per_us) - 1))]
 
     flops, nbytes = w.flops(), w.alg_bytes()
+    if args.path == "bwd":
+        # five products (recomputed S, dP, dV, dK, dQ) against the forward's two;
+        # bytes: read Q, K, V, O, dO, LSE, write dQ, dK, dV
+        flops = 2.5 * flops
+        n = w.B * w.H * w.S
+        nbytes = 16 * n * w.D + 4 * n
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (mean_us * 1e-6) / 1e12
     # the square D=128/512 causal shapes sit near the ridge; decode streams K/V
@@ -256,7 +304,9 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and not decode:
+    if not args.no_cpu_baseline and args.path == "bwd":
+        out["cpu_baseline"] = cpu_baseline_bwd(w, args.cpu_seconds)
+    elif not args.no_cpu_baseline and not decode:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

@@ -156,6 +156,35 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
                     int B, int H, int Sq, int Sk, int D, int causal, float scale, int splits,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward of attn_fwd for D = 64 or 128: the gradients of L = sum(dO * O)
+ * with respect to q, k and v ("Validating Memory-Optimal Transformer Kernels
+ * on Real Hardware", abstract and section 4, which measures this backward and
+ * its atomic-free rewrite):
+ *   P  = exp(scale Q K^T + mask - LSE)       (recomputed, never stored)
+ *   dV = P^T dO
+ *   dS = P * (dO V^T - rowsum(dO * O))
+ *   dQ = scale dS K,   dK = scale dS^T Q
+ *
+ *   q, k, v, o, dout : fp16 [B, H, S, D], device; o and lse are the outputs of
+ *                      attn_fwd for the same q, k, v, causal and scale
+ *   lse              : fp32 [B, H, S], device (natural log)
+ *   dq, dk, dv       : fp16 [B, H, S, D], device, written; they must not
+ *                      overlap each other or any input
+ *   workspace        : device memory of at least
+ *                      attn_bwd_workspace_bytes(B, H, S) bytes (2 floats per
+ *                      row), owned by the caller and overwritten
+ * Accumulation is fp32; P and dS are rounded to fp16 before the products
+ * that consume them.  Three launches on `stream`, asynchronous like
+ * attn_fwd; no atomics, so the outputs are deterministic.  Returns the same
+ * status codes as attn_fwd (ATTN_ERR_HEAD_DIM for D other than 64 or 128,
+ * ATTN_ERR_WORKSPACE for a missing or short workspace).
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int S);
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int B, int H, int S, int D,
+             int causal, float scale, void* workspace, size_t workspace_bytes, void* stream);
+
 /* 1 if attn_fwd accepts head dimension D, else 0. */
 int attn_head_dim_supported(int D);
 

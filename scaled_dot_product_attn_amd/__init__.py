@@ -14,13 +14,14 @@ import os
 from .build import LIB_PATH
 
 __all__ = ["AttnError", "fwd", "fwd_unfused", "unfused_workspace_bytes", "fwd_splitkv",
-           "splitkv_workspace_bytes", "fwd_decode", "decode_workspace_bytes", "decode_splits", "head_dim_supported", "load_library", "LIB_PATH",
+           "splitkv_workspace_bytes", "fwd_decode", "decode_workspace_bytes", "decode_splits", "bwd", "bwd_workspace_bytes", "head_dim_supported", "load_library", "LIB_PATH",
            "SYMBOLS"]
 
 # Every symbol include/attn.h declares.
 SYMBOLS = ("attn_fwd", "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
            "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
            "attn_fwd_decode", "attn_fwd_decode_workspace_bytes",
+           "attn_bwd", "attn_bwd_workspace_bytes",
            "attn_head_dim_supported", "attn_status_string", "attn_last_hip_error")
 
 ATTN_ERR_LAUNCH = -5
@@ -67,6 +68,10 @@ def load_library(path: str = LIB_PATH):
     L.attn_fwd_decode.restype = I
     L.attn_fwd_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     L.attn_fwd_decode_workspace_bytes.restype = Z
+    L.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, Z, P]
+    L.attn_bwd.restype = I
+    L.attn_bwd_workspace_bytes.argtypes = [I, I, I]
+    L.attn_bwd_workspace_bytes.restype = Z
     L.attn_head_dim_supported.argtypes = [I]
     L.attn_head_dim_supported.restype = I
     L.attn_status_string.argtypes = [I]
@@ -236,3 +241,38 @@ def fwd_decode(q, k, v, *, causal: bool, splits: int | None = None,
                              lse.data_ptr(), B, H, Sq, Sk, D, int(bool(causal)), float(scale),
                              int(splits), wptr, wbytes, stream))
     return out, lse
+
+
+def bwd_workspace_bytes(B: int, H: int, S: int) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(B, H, S))
+
+
+def bwd(q, k, v, o, lse, do, *, causal: bool, scale: float | None = None, dq=None, dk=None,
+        dv=None, workspace=None):
+    """Backward of fwd (D = 64 or 128): q, k, v, o, do contiguous fp16
+    [B, H, S, D] and lse fp32 [B, H, S] on one GPU, o and lse from fwd with the
+    same causal and scale.  Returns (dq, dk, dv), fp16 [B, H, S, D].
+    Enqueued on the current stream; asynchronous."""
+    import torch
+    B, H, S, D, _, _, scale, stream = _prepare(q, k, v, o, lse, scale)
+    if not isinstance(do, torch.Tensor) or do.dtype != torch.float16 or \
+            do.shape != q.shape or not do.is_contiguous() or do.device != q.device:
+        raise ValueError("do must be a contiguous float16 tensor shaped like q")
+    grads = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty_like(q)
+        elif t.shape != q.shape or t.dtype != torch.float16 or not t.is_contiguous() \
+                or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous float16 tensor shaped like q")
+        grads.append(t)
+    L = load_library()
+    need = bwd_workspace_bytes(B, H, S)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(L.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      do.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
+                      grads[2].data_ptr(), B, H, S, D, int(bool(causal)), scale,
+                      workspace.data_ptr(), wbytes, stream))
+    return tuple(grads)

@@ -152,6 +152,42 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
     return launched(attn::launch_decode(a));
 }
 
+size_t attn_bwd_workspace_bytes(int B, int H, int S) {
+    if (B < 1 || H < 1 || S < 1) return 0;
+    return (size_t)B * H * S * 2 * sizeof(float);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int B, int H, int S, int D,
+             int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
+    if (B < 1 || H < 1 || S < 1 || D < 1) return ATTN_ERR_SHAPE;
+    const long long bh = (long long)B * H;
+    // rows are indexed with 32-bit ints; one workgroup per (batch, head, 64-row tile)
+    if (bh > INT32_MAX || (long long)S > INT32_MAX / 2 || bh * S > INT32_MAX / 2 ||
+        bh * ((S + 63) / 64) > INT32_MAX)
+        return ATTN_ERR_SHAPE;
+    if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+    if (!isfinite(scale)) return ATTN_ERR_SCALE;
+    const size_t need = attn_bwd_workspace_bytes(B, H, S);
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    const size_t nt = (size_t)bh * S * D * 2, nl = (size_t)bh * S * 4;
+    const void* in[7] = {q, k, v, o, dout, lse, workspace};
+    const size_t in_n[7] = {nt, nt, nt, nt, nt, nl, need};
+    void* out[3] = {dq, dk, dv};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 7; ++j)
+            if (overlaps(out[i], nt, in[j], in_n[j])) return ATTN_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(out[i], nt, out[j], nt)) return ATTN_ERR_ALIAS;
+    }
+    for (int j = 0; j < 6; ++j)
+        if (overlaps(workspace, need, in[j], in_n[j])) return ATTN_ERR_ALIAS;
+    const attn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, B, H, S, D,
+                          causal != 0, scale, workspace, stream};
+    return launched(attn::launch_bwd(a));
+}
+
 const char* attn_status_string(int status) {
     switch (status) {
         case ATTN_OK: return "ok";

@@ -1,0 +1,521 @@
+// Attention backward for gfx950, D in {64, 128}: the gradients of
+// L = sum(dO * O) for O = softmax(scale Q K^T + causal mask) V, from the
+// forward's saved LSE (the probabilities are recomputed, never stored).
+//
+//   P[i,j]  = exp(scale q_i.k_j - LSE_i)            (0 where masked)
+//   Dlt[i]  = dO_i . O_i
+//   dP[i,j] = dO_i . v_j,   dS = P (dP - Dlt)
+//   dV = P^T dO,   dK = scale dS^T Q,   dQ = scale dS K
+//
+// "Validating Memory-Optimal Transformer Kernels on Real Hardware" (abstract
+// and section 4, "Paper II: Backward Pass and Fused Forward+Backward") measures
+// an attention backward that never materialises the O(n^2) probabilities and
+// traces its GPU cost to atomic updates of the key gradients (4.4 - 4.7).
+// Here there are no atomics at all, so the result is deterministic: three
+// launches,
+//   bwd_pre   : Dlt and LSE in log2 units per row, into the workspace;
+//   bwd_dkdv  : one workgroup per 64-key tile; it walks the query tiles that
+//               see it and accumulates dK and dV in registers;
+//   bwd_dq    : one workgroup per 64-row query tile; it walks the key tiles
+//               it sees and accumulates dQ.
+// Each output row is written by exactly one workgroup.
+//
+// Inside both: 4 waves, wave w = (lo = w & 1, hi = w >> 1).  All products run
+// on v_mfma_f32_32x32x16_f16 with fp32 accumulation; P and dS enter the MFMAs
+// as fp16 (round to nearest even), dQ/dK/dV are written as fp16.
+//   A[m][k]: lane holds m = n, k = 8g .. 8g+7
+//   B[k][n]: lane holds n = n, k = 8g .. 8g+7
+//   C[m][n]: register r holds m = 8(r/4) + 4g + r%4, n = n
+// (g = lane / 32, n = lane % 32).  A score accumulator's registers 8h .. 8h+7
+// are directly the next product's operand over the rows they index, with the
+// k order 16h + {4g .. 4g+3, 8+4g .. 8+4g+3}; the matching operand is read
+// from a row-major tile with ds_read_b64_tr_b16, as in the forward's P V.
+//
+// LDS tiles are read both ways (rows as an MFMA operand, and transposed), so
+// their 16-byte chunks are XOR-swizzled with a pattern that keeps both the
+// 16-row ds_read_b128 and the 4-row ds_read_b64_tr_b16 conflict-free.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fwd_common.h"
+#include "kernels.h"
+
+namespace attn {
+namespace {
+
+using namespace detail;
+
+template <int D>
+struct GeoB {
+    static constexpr int NW = 4, NT = 256, BT = 64;  // rows (or keys) per tile
+    static constexpr int CPR = D / 8;                // 16-byte chunks per row
+    static constexpr int TILE = BT * D;              // halfs of one swizzled tile
+    static constexpr int CH = BT * CPR / NT;         // chunks per thread per tile
+    static constexpr int NB = D / 32;
+    static_assert(D == 64 || D == 128, "D");
+    static_assert(CH * NT == BT * CPR, "tile split");
+};
+
+// XOR applied to the 16-byte chunk index of row r.  D = 128 (16 chunks, 256 B
+// per row): 4 (r & 3) | ((r >> 2) & 3) is a bijection on r mod 16, so 16
+// consecutive rows at one logical chunk hit 16 distinct chunk slots, and 4
+// consecutive rows (r0 = 0 mod 4) x 4 chunks 4b .. 4b+3 also map to 16
+// distinct slots.  D = 64 (8 chunks, 128 B per row, two rows per bank period):
+// 4 ((r >> 1) & 1) | ((r >> 2) & 3) does the same for rows of equal parity.
+template <int D>
+__device__ __forceinline__ int swz_b(int r) {
+    return D == 128 ? (4 * (r & 3)) | ((r >> 2) & 3) : (4 * ((r >> 1) & 1)) | ((r >> 2) & 3);
+}
+
+template <int D>
+struct Bwd {
+    using G = GeoB<D>;
+    static constexpr int NB = G::NB;
+
+    int S, tid, lane, g, n, lo, hi;
+    size_t base, row_base;  // element offset of this (batch, head); its first LSE row
+    float c;                // |scale| log2(e)
+    uint32_t qsign;         // 0x80008000 when the scale is negative
+
+    // Buffer over rows r0 .. r0+63 of t, clipped at S: reads past it return zero.
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const _Float16* t, int r0) const {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(t + base + (size_t)r0 * D),
+                                                 (short)0, min(max(S - r0, 0), 64) * D * 2, 0x00020000);
+    }
+    // Rows r0 .. r0+63 of t (past S read as zero) -> registers x[CH].
+    __device__ __forceinline__ void load(u32x4* x, const _Float16* t, int r0) const {
+        const auto r = rsrc(t, r0);
+#pragma unroll
+        for (int u = 0; u < G::CH; ++u)
+            x[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 r, 16 * (tid + G::NT * u), 0, 0));
+    }
+    __device__ __forceinline__ void store(_Float16* tile, const u32x4* x) const {
+#pragma unroll
+        for (int u = 0; u < G::CH; ++u) {
+            const int ci = tid + G::NT * u;
+            const int row = ci / G::CPR, cc = ci % G::CPR;
+            *reinterpret_cast<u32x4*>(tile + row * D + 8 * (cc ^ swz_b<D>(row))) = x[u];
+        }
+    }
+    // Row fragments of rows r0 .. r0+31 (A or B operand with the head dim as k):
+    // f[kk] = row (r0 + n), dims 16kk + 8g .. +7.
+    __device__ __forceinline__ void rows(half8* f, const _Float16* tile, int r0) const {
+        const int row = r0 + n;
+        const _Float16* p = tile + row * D;
+        const int sw = swz_b<D>(row);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            f[kk] = *reinterpret_cast<const half8*>(p + 8 * ((2 * kk + g) ^ sw));
+    }
+    // Transposed fragments of rows r0 .. r0+31 (the operand whose k runs over
+    // those rows): f[h][b] holds head dims 32b + (lane % 32) for rows
+    // r0 + 16h + {4g .. 4g+3, 8+4g .. 8+4g+3}.  In each 16-lane group lane
+    // 4r + c addresses row r, columns 4c .. 4c+3 and receives column
+    // lane % 16 of rows 0..3.
+    __device__ __forceinline__ void cols(half8 (*f)[NB], const _Float16* tile, int r0) const {
+        const int n16 = n >> 4, jj = n & 15;
+        const int sub = (jj & 3) >> 1, half = jj & 1;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                half4 part[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int row = r0 + 4 * g + (jj >> 2) + 16 * h + 8 * t;
+                    const int chunk = (4 * b + 2 * n16 + sub) ^ swz_b<D>(row);
+                    part[t] = __builtin_bit_cast(
+                        half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                                   (lds_half4*)(tile + row * D + 8 * chunk + 4 * half)));
+                }
+                f[h][b] = half8{part[0][0], part[0][1], part[0][2], part[0][3],
+                                part[1][0], part[1][1], part[1][2], part[1][3]};
+            }
+    }
+    // Fragment of rows (r0 + n) straight from global memory (rows past S read
+    // as zero); xsign flips fp16 signs.
+    __device__ __forceinline__ void grows(half8* f, const _Float16* t, int r0, uint32_t xsign) const {
+        const auto r = rsrc(t, r0);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    r, (n * D + 16 * kk + 8 * g) * 2, 0, 0));
+            x ^= xsign;
+            f[kk] = __builtin_bit_cast(half8, x);
+        }
+    }
+};
+
+// Dlt[i] = dO_i . O_i and LSE_i log2(e), one wave per row.
+template <int D>
+__global__ void __launch_bounds__(256)
+bwd_pre_kernel(const _Float16* __restrict__ O, const _Float16* __restrict__ dO,
+               const float* __restrict__ LSE, float* __restrict__ dlt, float* __restrict__ lse2,
+               long long rows)
+{
+    const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    const int lane = threadIdx.x & 63;
+    float acc = 0.f;
+    for (int d = lane; d < D; d += 64)
+        acc += (float)O[r * D + d] * (float)dO[r * D + d];
+#pragma unroll
+    for (int s = 32; s > 0; s >>= 1) acc += __shfl_xor(acc, s, 64);
+    if (lane == 0) {
+        dlt[r] = acc;
+        lse2[r] = LSE[r] * 1.44269504088896340736f;
+    }
+}
+
+// dK and dV for one 64-key tile.  Wave (lo, hi): keys 32lo .. +31 of the tile,
+// query rows 32hi .. +31 of every query tile that sees the keys.
+//   S  = Q K^T  : A = Q rows (LDS), B = this wave's K rows (registers)
+//   dP = dO V^T : A = dO rows (LDS), B = this wave's V rows (registers)
+//   dV += P^T dO, dK += dS^T Q : A = P^T / dS^T (score registers), B = dO / Q
+//                 columns (transposed LDS reads)
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1)
+bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
+                const _Float16* __restrict__ V, const _Float16* __restrict__ dO,
+                const float* __restrict__ dlt, const float* __restrict__ lse2,
+                _Float16* __restrict__ dK, _Float16* __restrict__ dV,
+                int BH, int S, float c, float scale, uint32_t qsign)
+{
+    using G = GeoB<D>;
+    constexpr int NB = G::NB;
+    // two stages of (Q tile, dO tile, lse2[64], dlt[64])
+    constexpr int STAGE = 2 * G::TILE + 2 * 64 * 2;  // halfs
+    __shared__ __attribute__((aligned(1024))) _Float16 lds[2 * STAGE];
+
+    const int T = (S + 63) / 64;
+    const int bh = blockIdx.x % BH;
+    const int kt = blockIdx.x / BH;  // causal: kt = 0 sees the most query tiles, so runs first
+    const int k0 = kt * 64;
+
+    Bwd<D> f;
+    f.S = S;
+    f.tid = threadIdx.x;
+    f.lane = threadIdx.x & 63;
+    f.g = f.lane >> 5;
+    f.n = f.lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    f.lo = w & 1;
+    f.hi = w >> 1;
+    f.base = (size_t)bh * S * D;
+    f.row_base = (size_t)bh * S;
+    f.c = c;
+    f.qsign = qsign;
+    const int lo = f.lo, hi = f.hi, g = f.g, n = f.n, lane = f.lane;
+
+    // this wave's K and V rows as B operands (k = head dim), kept for the whole walk
+    half8 kb[D / 16], vb[D / 16];
+    f.grows(kb, K, k0 + 32 * lo, qsign);  // a negative scale negates the logits
+    f.grows(vb, V, k0 + 32 * lo, 0u);
+
+    floatx16 dk[NB], dv[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            dk[b][r] = 0.f;
+            dv[b][r] = 0.f;
+        }
+
+    const int qt0 = CAUSAL ? kt : 0;
+    u32x4 xq[G::CH], xo[G::CH];
+    float lv = 0.f, dv_ = 0.f;
+    auto stage_of = [&](int s) { return lds + s * STAGE; };
+    auto fetch = [&](int qt) {
+        f.load(xq, Q, qt * 64);
+        f.load(xo, dO, qt * 64);
+        if (f.tid < 64) {
+            const int row = qt * 64 + f.tid;
+            lv = row < S ? lse2[f.row_base + row] : 0.f;
+            dv_ = row < S ? dlt[f.row_base + row] : 0.f;
+        }
+    };
+    auto put = [&](int s) {
+        _Float16* st = stage_of(s);
+        f.store(st, xq);
+        f.store(st + G::TILE, xo);
+        if (f.tid < 64) {
+            float* fl = reinterpret_cast<float*>(st + 2 * G::TILE);
+            fl[f.tid] = lv;
+            fl[64 + f.tid] = dv_;
+        }
+    };
+    fetch(qt0);
+    put(0);
+    int s = 0;
+    for (int qt = qt0; qt < T; ++qt) {
+        barrier();  // query tile qt is in stage s; every wave is done with qt-1
+        const bool more = qt + 1 < T;
+        if (more) fetch(qt + 1);
+        const _Float16* Qs = stage_of(s);
+        const _Float16* Os = Qs + G::TILE;
+        const float* fl = reinterpret_cast<const float*>(Qs + 2 * G::TILE);
+        const int q0 = qt * 64 + 32 * hi;  // first query row of this wave
+
+        half8 af[D / 16];
+        f.rows(af, Qs, 32 * hi);
+        floatx16 sacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk], kb[kk], sacc, 0, 0, 0);
+        f.rows(af, Os, 32 * hi);
+        floatx16 dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk], vb[kk], dp, 0, 0, 0);
+
+        // register r holds query q0 + 8(r/4) + 4g + r%4 for key k0 + 32lo + n
+        float4 l4[4], d4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            l4[j] = *reinterpret_cast<const float4*>(fl + 32 * hi + 8 * j + 4 * g);
+            d4[j] = *reinterpret_cast<const float4*>(fl + 64 + 32 * hi + 8 * j + 4 * g);
+        }
+        const int key = k0 + 32 * lo + n;
+        half8 pa[2], sa[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int qrow = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            const float lse_r = l4[r >> 2][r & 3], dlt_r = d4[r >> 2][r & 3];
+            const bool vis = qrow < S && key < S && (!CAUSAL || key <= qrow);
+            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -lse_r)) : 0.f;
+            const float ds = p * (dp[r] - dlt_r);
+            pa[r >> 3][r & 7] = (_Float16)p;
+            sa[r >> 3][r & 7] = (_Float16)ds;
+        }
+        half8 bf[2][NB];
+        f.cols(bf, Os, 32 * hi);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                dv[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[h], bf[h][b], dv[b], 0, 0, 0);
+        f.cols(bf, Qs, 32 * hi);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                dk[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[h], bf[h][b], dk[b], 0, 0, 0);
+        if (more) put(s ^ 1);
+        s ^= 1;
+    }
+
+    // the two query halves (hi = 0, 1) hold partial sums over disjoint rows:
+    // hi = 1 publishes, hi = 0 adds in a fixed order and writes
+    barrier();
+    float4* buf = reinterpret_cast<float4*>(lds) + lo * (2 * NB * 4) * 64;
+    if (hi == 1) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                buf[(4 * b + q4) * 64 + lane] =
+                    float4{dk[b][4 * q4], dk[b][4 * q4 + 1], dk[b][4 * q4 + 2], dk[b][4 * q4 + 3]};
+                buf[(4 * (NB + b) + q4) * 64 + lane] =
+                    float4{dv[b][4 * q4], dv[b][4 * q4 + 1], dv[b][4 * q4 + 2], dv[b][4 * q4 + 3]};
+            }
+    }
+    barrier();
+    if (hi == 1) return;
+    // register r of block b: key k0 + 32lo + 8(r/4) + 4g + r%4, head dim 32b + n
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 pk = buf[(4 * b + q4) * 64 + lane];
+            const float4 pv = buf[(4 * (NB + b) + q4) * 64 + lane];
+            const float sk[4] = {pk.x, pk.y, pk.z, pk.w}, sv[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int key = k0 + 32 * lo + 8 * q4 + 4 * g + e;
+                if (key < S) {
+                    const size_t at = f.base + (size_t)key * D + 32 * b + n;
+                    dK[at] = (_Float16)((dk[b][4 * q4 + e] + sk[e]) * scale);
+                    dV[at] = (_Float16)(dv[b][4 * q4 + e] + sv[e]);
+                }
+            }
+        }
+}
+
+// dQ for one 64-row query tile.  Wave (lo, hi): query rows 32lo .. +31 of the
+// tile, keys 32hi .. +31 of every key tile the rows see.
+//   S^T  = K Q^T  : A = K rows (LDS), B = this wave's Q rows (registers)
+//   dP^T = V dO^T : A = V rows (LDS), B = this wave's dO rows (registers)
+//   dQ  += dS K   : A = dS (score registers: lane = query, registers = keys),
+//                   B = K columns (transposed LDS reads)
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1)
+bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
+              const _Float16* __restrict__ V, const _Float16* __restrict__ dO,
+              const float* __restrict__ dlt, const float* __restrict__ lse2,
+              _Float16* __restrict__ dQ, int BH, int S, float c, float scale, uint32_t qsign)
+{
+    using G = GeoB<D>;
+    constexpr int NB = G::NB;
+    constexpr int STAGE = 2 * G::TILE;  // K tile, V tile
+    __shared__ __attribute__((aligned(1024))) _Float16 lds[2 * STAGE];
+
+    const int T = (S + 63) / 64;
+    const int bh = blockIdx.x % BH;
+    const int qt = CAUSAL ? T - 1 - blockIdx.x / BH : blockIdx.x / BH;  // heaviest first
+
+    Bwd<D> f;
+    f.S = S;
+    f.tid = threadIdx.x;
+    f.lane = threadIdx.x & 63;
+    f.g = f.lane >> 5;
+    f.n = f.lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    f.lo = w & 1;
+    f.hi = w >> 1;
+    f.base = (size_t)bh * S * D;
+    f.row_base = (size_t)bh * S;
+    f.c = c;
+    f.qsign = qsign;
+    const int lo = f.lo, hi = f.hi, g = f.g, n = f.n, lane = f.lane;
+
+    const int qrow = qt * 64 + 32 * lo + n;  // the query this lane owns
+    half8 qb[D / 16], ob[D / 16];
+    f.grows(qb, Q, qt * 64 + 32 * lo, qsign);
+    f.grows(ob, dO, qt * 64 + 32 * lo, 0u);
+    const float lse_q = qrow < S ? lse2[f.row_base + qrow] : 0.f;
+    const float dlt_q = qrow < S ? dlt[f.row_base + qrow] : 0.f;
+
+    floatx16 dq[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dq[b][r] = 0.f;
+
+    const int nT = CAUSAL ? qt + 1 : T;
+    u32x4 xk[G::CH], xv[G::CH];
+    f.load(xk, K, 0);
+    f.load(xv, V, 0);
+    f.store(lds, xk);
+    f.store(lds + G::TILE, xv);
+    int s = 0;
+    for (int kt = 0; kt < nT; ++kt) {
+        barrier();
+        const bool more = kt + 1 < nT;
+        if (more) {
+            f.load(xk, K, (kt + 1) * 64);
+            f.load(xv, V, (kt + 1) * 64);
+        }
+        const _Float16* Ks = lds + s * STAGE;
+        const _Float16* Vs = Ks + G::TILE;
+        const int k0 = kt * 64 + 32 * hi;  // first key of this wave
+
+        half8 af[D / 16];
+        f.rows(af, Ks, 32 * hi);
+        floatx16 sacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk], qb[kk], sacc, 0, 0, 0);
+        f.rows(af, Vs, 32 * hi);
+        floatx16 dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk], ob[kk], dp, 0, 0, 0);
+
+        // register r holds key k0 + 8(r/4) + 4g + r%4 for this lane's query
+        half8 sa[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            const bool vis = qrow < S && key < S && (!CAUSAL || key <= qrow);
+            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -lse_q)) : 0.f;
+            sa[r >> 3][r & 7] = (_Float16)(p * (dp[r] - dlt_q));
+        }
+        half8 bf[2][NB];
+        f.cols(bf, Ks, 32 * hi);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                dq[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[h], bf[h][b], dq[b], 0, 0, 0);
+        if (more) {
+            f.store(lds + (s ^ 1) * STAGE, xk);
+            f.store(lds + (s ^ 1) * STAGE + G::TILE, xv);
+        }
+        s ^= 1;
+    }
+
+    // the two key halves (hi = 0, 1) hold partial sums over disjoint keys
+    barrier();
+    float4* buf = reinterpret_cast<float4*>(lds) + lo * (NB * 4) * 64;
+    if (hi == 1) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                buf[(4 * b + q4) * 64 + lane] =
+                    float4{dq[b][4 * q4], dq[b][4 * q4 + 1], dq[b][4 * q4 + 2], dq[b][4 * q4 + 3]};
+    }
+    barrier();
+    if (hi == 1) return;
+    // register r of block b: query qt*64 + 32lo + 8(r/4) + 4g + r%4, head dim 32b + n
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 pq = buf[(4 * b + q4) * 64 + lane];
+            const float sq[4] = {pq.x, pq.y, pq.z, pq.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = qt * 64 + 32 * lo + 8 * q4 + 4 * g + e;
+                if (row < S)
+                    dQ[f.base + (size_t)row * D + 32 * b + n] = (_Float16)((dq[b][4 * q4 + e] + sq[e]) * scale);
+            }
+        }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_t(const BwdArgs& a) {
+    const int BH = a.B * a.H;
+    const int T = (a.S + 63) / 64;
+    const long long rows = (long long)BH * a.S;
+    float* dlt = (float*)a.workspace;
+    float* lse2 = dlt + rows;
+    // the sign of the scale is applied to Q/K (fp16 sign flip), its magnitude
+    // in c for the logits and in the final dQ/dK scaling
+    const float c = fabsf(a.scale) * 1.44269504088896340736f;
+    const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
+    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                       (hipStream_t)a.stream, (const _Float16*)a.o, (const _Float16*)a.dout, a.lse,
+                       dlt, lse2, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((long long)BH * T)), dim3(256), 0,
+                       (hipStream_t)a.stream, (const _Float16*)a.q, (const _Float16*)a.k,
+                       (const _Float16*)a.v, (const _Float16*)a.dout, dlt, lse2,
+                       (_Float16*)a.dk, (_Float16*)a.dv, BH, a.S, c, a.scale, qsign);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)BH * T)), dim3(256), 0,
+                       (hipStream_t)a.stream, (const _Float16*)a.q, (const _Float16*)a.k,
+                       (const _Float16*)a.v, (const _Float16*)a.dout, dlt, lse2,
+                       (_Float16*)a.dq, BH, a.S, c, a.scale, qsign);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a) {
+    if (a.D == 64) return a.causal ? launch_bwd_t<64, true>(a) : launch_bwd_t<64, false>(a);
+    return a.causal ? launch_bwd_t<128, true>(a) : launch_bwd_t<128, false>(a);
+}
+
+}  // namespace attn

@@ -56,4 +56,25 @@ hipError_t launch_unfused(const FwdArgs& a, void* workspace);
 // Row stride (elements) of the unfused workspace matrices: S rounded up to 64.
 int unfused_row_stride(int S);
 
+// Backward, D = 64 or 128: dQ, dK, dV (fp16) from Q, K, V, the forward's O
+// and LSE, and dO.  `workspace` holds 2 B H S floats (dO.O per row, LSE in
+// log2 units).  Three launches on a.stream, no atomics.
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const float* lse;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    int B, H, S, D;
+    int causal;
+    float scale;
+    void* workspace;
+    void* stream;
+};
+hipError_t launch_bwd(const BwdArgs& a);
+
 }  // namespace attn

@@ -186,3 +186,38 @@ def test_decode_validation(L):
     assert dec(lse=O) == C["ATTN_ERR_ALIAS"]
     # one chunk per query tile needs no workspace
     assert L.attn_fwd_decode_workspace_bytes(1, 2, 1, 4096, 128, 1, 1) == 0
+
+
+def test_bwd_workspace_bytes(L):
+    assert L.attn_bwd_workspace_bytes(2, 3, 1000) == 2 * 3 * 1000 * 2 * 4
+    assert L.attn_bwd_workspace_bytes(0, 3, 1000) == 0
+
+
+def test_bwd_validation(L):
+    B, H, S, D = 1, 2, 1024, 128
+    nt = B * H * S * D * 2
+    # fake, disjoint device addresses: validation never dereferences them
+    base = 0x80000000
+    q, k, v, o, do, dq, dk, dv = (base + i * nt for i in range(8))
+    lse = base + 8 * nt
+    ws = lse + B * H * S * 4
+    need = L.attn_bwd_workspace_bytes(B, H, S)
+    def bwd(q=q, k=k, v=v, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv, B=B, H=H, S=S, D=D,
+            causal=1, scale=0.1, ws=ws, wb=need):
+        return L.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, B, H, S, D, causal, scale, ws, wb,
+                          None)
+    assert bwd(q=None) == C["ATTN_ERR_NULL"]
+    assert bwd(do=None) == C["ATTN_ERR_NULL"]
+    assert bwd(dv=None) == C["ATTN_ERR_NULL"]
+    assert bwd(S=0) == C["ATTN_ERR_SHAPE"]
+    assert bwd(D=512) == C["ATTN_ERR_HEAD_DIM"]
+    assert bwd(D=96) == C["ATTN_ERR_HEAD_DIM"]
+    assert bwd(scale=math.inf) == C["ATTN_ERR_SCALE"]
+    assert bwd(ws=None) == C["ATTN_ERR_WORKSPACE"]
+    assert bwd(wb=need - 1) == C["ATTN_ERR_WORKSPACE"]
+    assert bwd(dq=k) == C["ATTN_ERR_ALIAS"]          # output over an input
+    assert bwd(dk=dq) == C["ATTN_ERR_ALIAS"]         # outputs over each other
+    assert bwd(dv=dq + 2) == C["ATTN_ERR_ALIAS"]     # partial overlap
+    assert bwd(ws=o) == C["ATTN_ERR_ALIAS"]          # workspace over an input
+    assert bwd(ws=dk) == C["ATTN_ERR_ALIAS"]         # workspace over an output
+    assert bwd(lse=dv) == C["ATTN_ERR_ALIAS"]
