@@ -172,10 +172,10 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
  *   dq, dk, dv       : fp16 [B, H, S, D], device, written; they must not
  *                      overlap each other or any input
  *   workspace        : device memory of at least
- *                      attn_bwd_workspace_bytes(B, H, S) bytes (2 floats per
- *                      row), owned by the caller and overwritten
+ *                      attn_bwd_workspace_bytes(B, H, S) bytes (one float
+ *                      per row), owned by the caller and overwritten
  * Accumulation is fp32; P and dS are rounded to fp16 before the products
- * that consume them.  Three launches on `stream`, asynchronous like
+ * that consume them.  Two launches on `stream`, asynchronous like
  * attn_fwd; no atomics, so the outputs are deterministic.  Returns the same
  * status codes as attn_fwd (ATTN_ERR_HEAD_DIM for D other than 64 or 128,
  * ATTN_ERR_WORKSPACE for a missing or short workspace).

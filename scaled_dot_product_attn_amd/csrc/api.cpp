@@ -154,7 +154,7 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
 
 size_t attn_bwd_workspace_bytes(int B, int H, int S) {
     if (B < 1 || H < 1 || S < 1) return 0;
-    return (size_t)B * H * S * 2 * sizeof(float);
+    return (size_t)B * H * S * sizeof(float);  // dO . O per row
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

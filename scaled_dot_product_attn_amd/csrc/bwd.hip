@@ -11,13 +11,13 @@
 // and section 4, "Paper II: Backward Pass and Fused Forward+Backward") measures
 // an attention backward that never materialises the O(n^2) probabilities and
 // traces its GPU cost to atomic updates of the key gradients (4.4 - 4.7).
-// Here there are no atomics at all, so the result is deterministic: three
+// Here there are no atomics at all, so the result is deterministic: two
 // launches,
-//   bwd_pre   : Dlt and LSE in log2 units per row, into the workspace;
+//   bwd_dq    : one workgroup per 64-row query tile; it forms Dlt for its rows
+//               (kept in the workspace for the next launch), walks the key
+//               tiles the rows see and accumulates dQ;
 //   bwd_dkdv  : one workgroup per 64-key tile; it walks the query tiles that
-//               see it and accumulates dK and dV in registers;
-//   bwd_dq    : one workgroup per 64-row query tile; it walks the key tiles
-//               it sees and accumulates dQ.
+//               see it and accumulates dK and dV in registers.
 // Each output row is written by exactly one workgroup.
 //
 // Inside both: 4 waves, wave w = (lo = w & 1, hi = w >> 1).  All products run
@@ -44,6 +44,8 @@ namespace attn {
 namespace {
 
 using namespace detail;
+
+constexpr float kLog2e = 1.44269504088896340736f;
 
 template <int D>
 struct GeoB {
@@ -147,27 +149,6 @@ struct Bwd {
     }
 };
 
-// Dlt[i] = dO_i . O_i and LSE_i log2(e), one wave per row.
-template <int D>
-__global__ void __launch_bounds__(256)
-bwd_pre_kernel(const _Float16* __restrict__ O, const _Float16* __restrict__ dO,
-               const float* __restrict__ LSE, float* __restrict__ dlt, float* __restrict__ lse2,
-               long long rows)
-{
-    const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= rows) return;
-    const int lane = threadIdx.x & 63;
-    float acc = 0.f;
-    for (int d = lane; d < D; d += 64)
-        acc += (float)O[r * D + d] * (float)dO[r * D + d];
-#pragma unroll
-    for (int s = 32; s > 0; s >>= 1) acc += __shfl_xor(acc, s, 64);
-    if (lane == 0) {
-        dlt[r] = acc;
-        lse2[r] = LSE[r] * 1.44269504088896340736f;
-    }
-}
-
 // dK and dV for one 64-key tile.  Wave (lo, hi): keys 32lo .. +31 of the tile,
 // query rows 32hi .. +31 of every query tile that sees the keys.
 //   S  = Q K^T  : A = Q rows (LDS), B = this wave's K rows (registers)
@@ -178,13 +159,13 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 1)
 bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                 const _Float16* __restrict__ V, const _Float16* __restrict__ dO,
-                const float* __restrict__ dlt, const float* __restrict__ lse2,
+                const float* __restrict__ dlt, const float* __restrict__ LSE,
                 _Float16* __restrict__ dK, _Float16* __restrict__ dV,
                 int BH, int S, float c, float scale, uint32_t qsign)
 {
     using G = GeoB<D>;
     constexpr int NB = G::NB;
-    // two stages of (Q tile, dO tile, lse2[64], dlt[64])
+    // two stages of (Q tile, dO tile, LSE log2(e) [64], dlt[64])
     constexpr int STAGE = 2 * G::TILE + 2 * 64 * 2;  // halfs
     __shared__ __attribute__((aligned(1024))) _Float16 lds[2 * STAGE];
 
@@ -231,7 +212,7 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
         f.load(xo, dO, qt * 64);
         if (f.tid < 64) {
             const int row = qt * 64 + f.tid;
-            lv = row < S ? lse2[f.row_base + row] : 0.f;
+            lv = row < S ? LSE[f.row_base + row] * kLog2e : 0.f;
             dv_ = row < S ? dlt[f.row_base + row] : 0.f;
         }
     };
@@ -356,8 +337,9 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 1)
 bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
               const _Float16* __restrict__ V, const _Float16* __restrict__ dO,
-              const float* __restrict__ dlt, const float* __restrict__ lse2,
-              _Float16* __restrict__ dQ, int BH, int S, float c, float scale, uint32_t qsign)
+              const _Float16* __restrict__ O, const float* __restrict__ LSE,
+              float* __restrict__ dlt, _Float16* __restrict__ dQ, int BH, int S, float c,
+              float scale, uint32_t qsign)
 {
     using G = GeoB<D>;
     constexpr int NB = G::NB;
@@ -387,8 +369,21 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     half8 qb[D / 16], ob[D / 16];
     f.grows(qb, Q, qt * 64 + 32 * lo, qsign);
     f.grows(ob, dO, qt * 64 + 32 * lo, 0u);
-    const float lse_q = qrow < S ? lse2[f.row_base + qrow] : 0.f;
-    const float dlt_q = qrow < S ? dlt[f.row_base + qrow] : 0.f;
+    const float lse_q = qrow < S ? LSE[f.row_base + qrow] * kLog2e : 0.f;
+    // Dlt = dO . O of this lane's query: each half of the wave holds half of
+    // the head dims (8g .. 8g+7 of every 16)
+    float dlt_q;
+    {
+        half8 of[D / 16];
+        f.grows(of, O, qt * 64 + 32 * lo, 0u);
+        float acc = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)of[kk][e], (float)ob[kk][e], acc);
+        dlt_q = sum_halves(acc);
+        if (hi == 0 && g == 0 && qrow < S) dlt[f.row_base + qrow] = dlt_q;
+    }
 
     floatx16 dq[NB];
 #pragma unroll
@@ -486,28 +481,23 @@ template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs& a) {
     const int BH = a.B * a.H;
     const int T = (a.S + 63) / 64;
-    const long long rows = (long long)BH * a.S;
     float* dlt = (float*)a.workspace;
-    float* lse2 = dlt + rows;
     // the sign of the scale is applied to Q/K (fp16 sign flip), its magnitude
     // in c for the logits and in the final dQ/dK scaling
-    const float c = fabsf(a.scale) * 1.44269504088896340736f;
+    const float c = fabsf(a.scale) * kLog2e;
     const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
-    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
-                       (hipStream_t)a.stream, (const _Float16*)a.o, (const _Float16*)a.dout, a.lse,
-                       dlt, lse2, rows);
+    const dim3 grid((unsigned)((long long)BH * T));
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), grid, dim3(256), 0, (hipStream_t)a.stream,
+                       (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,
+                       (const _Float16*)a.dout, (const _Float16*)a.o, a.lse, dlt,
+                       (_Float16*)a.dq, BH, a.S, c, a.scale, qsign);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((long long)BH * T)), dim3(256), 0,
-                       (hipStream_t)a.stream, (const _Float16*)a.q, (const _Float16*)a.k,
-                       (const _Float16*)a.v, (const _Float16*)a.dout, dlt, lse2,
-                       (_Float16*)a.dk, (_Float16*)a.dv, BH, a.S, c, a.scale, qsign);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)BH * T)), dim3(256), 0,
-                       (hipStream_t)a.stream, (const _Float16*)a.q, (const _Float16*)a.k,
-                       (const _Float16*)a.v, (const _Float16*)a.dout, dlt, lse2,
-                       (_Float16*)a.dq, BH, a.S, c, a.scale, qsign);
+    // reads the Dlt rows that bwd_dq wrote (same stream, so after it)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), grid, dim3(256), 0, (hipStream_t)a.stream,
+                       (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,
+                       (const _Float16*)a.dout, dlt, a.lse, (_Float16*)a.dk, (_Float16*)a.dv,
+                       BH, a.S, c, a.scale, qsign);
     return hipGetLastError();
 }
 

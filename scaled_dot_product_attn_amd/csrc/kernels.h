@@ -57,8 +57,8 @@ hipError_t launch_unfused(const FwdArgs& a, void* workspace);
 int unfused_row_stride(int S);
 
 // Backward, D = 64 or 128: dQ, dK, dV (fp16) from Q, K, V, the forward's O
-// and LSE, and dO.  `workspace` holds 2 B H S floats (dO.O per row, LSE in
-// log2 units).  Three launches on a.stream, no atomics.
+// and LSE, and dO.  `workspace` holds B H S floats (dO.O per row).  Two
+// launches on a.stream, no atomics.
 struct BwdArgs {
     const void* q;
     const void* k;

@@ -189,7 +189,7 @@ def test_decode_validation(L):
 
 
 def test_bwd_workspace_bytes(L):
-    assert L.attn_bwd_workspace_bytes(2, 3, 1000) == 2 * 3 * 1000 * 2 * 4
+    assert L.attn_bwd_workspace_bytes(2, 3, 1000) == 2 * 3 * 1000 * 4
     assert L.attn_bwd_workspace_bytes(0, 3, 1000) == 0
 
 
