@@ -343,9 +343,9 @@ int oracle_softmax_av_f64(const double *logits, const uint16_t *v16, double *o,
  *   dS[i,j] = P[i,j] (dP[i,j] - Dlt[i])
  *   dQ[i]   = scale sum_j dS[i,j] k[j],   dK[j] = scale sum_i dS[i,j] q[i]
  * The step after the forward ("Validating Memory-Optimal Transformer Kernels
- * on Real Hardware", sections 1.2 and 4: the backward kernel and the fused
- * forward+backward that avoid the O(n^2) intermediate); the chain rule of the
- * softmax is the plain one.  q, k, v, dO: fp16 bits [B, H, S, D];
+ * on Real Hardware", abstract and section 4: the backward kernel and the
+ * fused forward+backward that avoid the O(n^2) intermediate); the chain rule
+ * of the softmax is the plain one.  q, k, v, dO: fp16 bits [B, H, S, D];
  * dq, dk, dv: float64 [B, H, S, D], overwritten.  Sums run in index order;
  * heads are independent and OpenMP splits over heads only.
  * `mistake` (0 = as specified) plants one error for the pins' power tests:
