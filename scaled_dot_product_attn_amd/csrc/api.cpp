@@ -55,7 +55,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     if (st != ATTN_OK) return st;
     const attn::FwdArgs a{q, k, v, o, lse, B, H, S, D, causal != 0, scale, stream};
     if (D == 512) return launched(attn::launch_fused_d512(a));
-    return launched(attn::launch_fused_pair8_d64_d128(a));
+    return launched(attn::launch_fused_pipe_d64_d128(a));
 }
 
 size_t attn_fwd_unfused_workspace_bytes(int B, int H, int S) {

@@ -1,0 +1,480 @@
+// Fused attention forward for gfx950, D in {64, 128}: one workgroup of four
+// waves per 64-row query tile, two workgroups per CU, with the next key
+// tile's Q K^T on the matrix cores while the vector ALUs run the current
+// tile's softmax.
+//
+//   O = softmax(scale * Q K^T + causal mask) V,   LSE = log sum_j exp(scale q.k_j)
+//
+// The score tile lives only in registers ("An Optimal Mapper Meets a Real
+// GPU", section "Ground rules": one fused kernel instead of a pipeline of
+// kernels through global workspaces).
+//
+// Wave w takes query rows 32(w&1) .. +31 of the tile against keys
+// 32(w>>1) .. +31 of every 64-key tile; the two key halves are merged in LDS
+// at the end (an online-softmax merge over disjoint key sets, exact up to
+// rounding, fixed order).
+//
+// Software pipeline, per key tile j of a wave:
+//     S(j+1) = K(j+1) Q^T        matrix cores   \  issued together, no
+//     P(j)   = softmax(S(j))     vector ALUs    /  dependence between them
+//     O     += V(j)^T P(j)       matrix cores
+// so K runs one tile ahead of V.  K and V tiles go from global memory
+// straight into LDS (buffer loads with the LDS destination bit: no
+// registers, no LDS write instructions), into two K slots and two V slots,
+// each a separate LDS array.  Iteration j starts with the K(j+1) and V(j)
+// fragments in registers and the loads of K(j+2) and V(j+1) in flight;
+// after S(j+1) and the softmax of S(j) every wave waits for its loads and
+// meets the barrier, then issues the loads of K(j+3) over K(j+1) and V(j+2)
+// over V(j) (both read before the barrier), reads the K(j+2) fragments, runs
+// O += V(j)^T P(j) while they arrive, and reads the V(j+1) fragments.  No
+// LDS latency sits between the barrier and the next matrix instruction.
+//
+// The K slots are XOR-swizzled by row (no padding, so that a 1 KB load
+// lands as whole rows), the V slots as for the transposed reads.
+//
+// MFMA lane layouts (v_mfma_f32_32x32x16_f16, wave64, g = lane / 32,
+// n = lane % 32):
+//   A[m][k]: lane holds m = n, k = 8g .. 8g+7
+//   B[k][n]: lane holds n = n, k = 8g .. 8g+7
+//   C[m][n]: register r holds m = 8(r/4) + 4g + r%4, n = n
+// S^T = K Q^T puts one query per lane (n) and 16 of the wave's 32 keys in
+// its registers; O^T += V^T P^T takes P^T straight from those registers as
+// the B operand and V^T from transposed LDS reads (ds_read_b64_tr_b16).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fwd_common.h"
+#include "kernels.h"
+
+namespace attn {
+namespace {
+
+using namespace detail;
+
+template <int D>
+struct GeoP {
+    static constexpr int NW = 4;                 // waves per workgroup
+    static constexpr int NT = 64 * NW;           // threads
+    static constexpr int BM = 64;                // query rows per tile
+    static constexpr int BN = 64;                // keys per tile
+    static constexpr int CPR = D / 8;            // 16-byte chunks per row
+    static constexpr int TILE = BN * D;          // halfs of a K or V slot (swizzled, no pad)
+    static constexpr int PIECES = TILE * 2 / 1024 / NW;  // 1 KB DMA pieces per wave per tile
+    static constexpr int ROWS_PER_PIECE = 1024 / (D * 2);
+    static constexpr int SLOT = 16 * D + 128;    // floats of one wave's merge slot
+    static_assert(D == 64 || D == 128, "D");
+    static_assert(PIECES * NW * 1024 == TILE * 2, "tile split into 1 KB pieces");
+    static_assert(4 * TILE * 2 * 2 <= 160 * 1024, "LDS budget for two workgroups per CU");
+    static_assert(SLOT * 4 <= TILE * 2, "a merge slot fits one tile array");
+};
+
+// K slot swizzle (16-byte chunk index XOR): the 16 rows that one group of 16
+// lanes reads at a common logical chunk land on 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// V slot swizzle: 16-byte chunk index XOR, so that the lanes of a transposed
+// read hit distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_vp(int r) {
+    return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+// Online softmax of one 32-key x 32-query S^T block (register r of lane
+// (g, n): key 8(r/4) + 4g + r%4 of the block, query n; keys with
+// 8(r/4) + r%4 > lim are masked when MASK).  c = |scale| log2(e); m: the
+// running reference max (log2 units), l: this lane's share of the row sum,
+// o: the output blocks.  P^T (fp16, round to nearest even) goes to pf as the
+// B operand of the two 16-key P V steps.
+//
+// The weights are formed against the current reference max before the row
+// max is known; only when the row max outgrows the reference by more than
+// 2^kLazyTau are the output and sum rescaled and the weights formed again.
+// Max and sum run as trees (short dependence chains), and the speculative
+// weights are pinned ahead of the branch so that they stay in the same
+// scheduling region as the next tile's matrix instructions.
+template <bool MASK, int NB, bool PIPE>
+__device__ __forceinline__ void softmax_block(floatx16 s, int lim, float c, float& m, float& l,
+                                              floatx16* o, half8* pf) {
+    if (MASK) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if ((8 * (r >> 2) + (r & 3)) > lim) s[r] = kNegInf;
+    }
+    const float mx = fmaxf(fmaxf(fmaxf(fmaxf(s[0], s[1]), s[2]), fmaxf(fmaxf(s[3], s[4]), s[5])),
+                           fmaxf(fmaxf(fmaxf(s[6], s[7]), s[8]),
+                                 fmaxf(fmaxf(fmaxf(s[9], s[10]), s[11]),
+                                       fmaxf(fmaxf(fmaxf(s[12], s[13]), s[14]), s[15]))));
+    // weights against reference mref: P^T in fp16 into pf, and this lane's
+    // sum in fp32 (four partial sums, then a tree)
+    auto weights = [&](float mref) {
+        float q[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float t = __builtin_fmaf(s[r], c, -mref);
+            if (MASK && (8 * (r >> 2) + (r & 3)) > lim) t = kNegInf;
+            const float e = __builtin_amdgcn_exp2f(t);
+            q[r & 3] += e;
+            pf[r >> 3][r & 7] = (_Float16)e;
+        }
+        return (q[0] + q[1]) + (q[2] + q[3]);
+    };
+    float psum = weights(m);
+    // keep the speculative weights ahead of the branch
+    asm volatile("" : "+v"(psum));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        u32x4 x = __builtin_bit_cast(u32x4, pf[h]);
+        asm volatile("" : "+v"(x));
+        pf[h] = __builtin_bit_cast(half8, x);
+    }
+    const float mxh = max_halves(mx);
+    if (PIPE) {
+        // interleave the next tile's Q K^T (8 MFMAs, issued by the caller in
+        // this region) with this softmax's vector work
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+        }
+    }
+    // fmaxf keeps the candidate finite when every key is masked (c * -inf)
+    // or c == 0 (0 * -inf)
+    const float cand = fmaxf(c * mxh, -kFltMax);
+    if (__builtin_amdgcn_ballot_w64(cand > m + kLazyTau) != 0) {
+        const float m_new = fmaxf(m, cand);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        m = m_new;
+        l *= alpha;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
+        psum = weights(m);
+    }
+    l += psum;
+}
+
+// The four LDS tile arrays of a workgroup: two K slots and two V slots.
+// They are separate objects so that the compiler can tell a DMA into one
+// from a read of another and never waits for the former before the latter.
+template <int D>
+struct Slots {
+    _Float16* k[2];
+    _Float16* v[2];
+};
+
+template <int D, bool CAUSAL>
+struct Pipe {
+    using G = GeoP<D>;
+    static constexpr int NB = D / 32;
+    using LdsPtr = __attribute__((address_space(3))) void*;
+
+    const _Float16* __restrict__ Q;
+    const _Float16* __restrict__ K;
+    const _Float16* __restrict__ V;
+    _Float16* __restrict__ O;
+    float* __restrict__ LSE;
+    Slots<D> sl;
+    int S;
+    size_t base, lse_base;
+    float c;
+    uint32_t qsign;
+    int tid, lane, g, n, w, rg, kh;
+
+    // Buffer over rows j0 .. min(j0 + 64, S) - 1 of t: reads past them return zero.
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const _Float16* t, int j0) const {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(t + base + (size_t)j0 * D),
+                                                 (short)0, min(S - j0, G::BN) * D * 2, 0x00020000);
+    }
+    // Tile j of t straight into an LDS slot (global -> LDS, no registers).
+    // This wave writes PIECES 1 KB pieces; lane L of a piece lands at byte
+    // 16 L of it, i.e. row ROWS_PER_PIECE * piece + L / CPR at physical chunk
+    // L % CPR, so it loads the logical chunk that the swizzle puts there.
+    __device__ __forceinline__ void dma(_Float16* slot, const _Float16* t, int j, bool isk) const {
+        const auto r = tile_rsrc(t, j * G::BN);
+#pragma unroll
+        for (int u = 0; u < G::PIECES; ++u) {
+            const int piece = w * G::PIECES + u;
+            const int row = G::ROWS_PER_PIECE * piece + lane / G::CPR;
+            const int phys = lane % G::CPR;
+            const int logical = phys ^ (isk ? swz_k<D>(row) : swz_vp<D>(row));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (LdsPtr)(slot + piece * 512), 16, (row * D + 8 * logical) * 2, 0, 0, 0);
+        }
+    }
+    // K fragments of keys 32kh .. +31 (A operand of S^T = K Q^T)
+    __device__ __forceinline__ void read_k(half8* kf, const _Float16* slot) const {
+        const int row = 32 * kh + n;
+        const _Float16* kp = slot + row * D;
+        const int sw = swz_k<D>(row);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            kf[kk] = *reinterpret_cast<const half8*>(kp + 8 * ((2 * kk + g) ^ sw));
+    }
+    // V^T fragments of keys 32kh .. +31: vf[h][b] covers keys 32kh + 16h .. +15
+    // and head dims 32b .. +31.  In each 16-lane group lane 4r + c addresses
+    // row r, columns 4c .. 4c+3 of a transposed read and receives column
+    // lane % 16 of rows 0..3, so two reads give the accumulator's key order
+    // 8(r/4) + 4g + r%4.
+    __device__ __forceinline__ void read_v(half8 (*vf)[NB], const _Float16* slot) const {
+        const int n16 = n >> 4, jj = n & 15;
+        const int sub = (jj & 3) >> 1, half = (jj & 1);
+        const int sw = swz_vp<D>(jj >> 2);  // row & 3 == jj >> 2 for every read below
+        const _Float16* rowp = slot + (32 * kh + 4 * g + (jj >> 2)) * D + 4 * half;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const _Float16* pb = rowp + 8 * ((4 * b + 2 * n16 + sub) ^ sw);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                half4 part[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    part[t] = __builtin_bit_cast(
+                        half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                                   (lds_half4*)(pb + (16 * h + 8 * t) * D)));
+                vf[h][b] = half8{part[0][0], part[0][1], part[0][2], part[0][3],
+                                 part[1][0], part[1][1], part[1][2], part[1][3]};
+            }
+        }
+    }
+    __device__ __forceinline__ floatx16 qk(const half8* kf, const half8* qf) const {
+        floatx16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kk], qf[kk], acc, 0, 0, 0);
+        return acc;
+    }
+    __device__ __forceinline__ void pv(floatx16* o, const half8 (*vf)[NB], const half8* pf) const {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[h][b], pf[h], o[b], 0, 0, 0);
+    }
+    // Barrier after this wave's DMA writes and LDS accesses have landed.
+    __device__ __forceinline__ void barrier_dma() const {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    }
+
+    // Iteration j (P = j & 1), entered with K(j+1) and V(j) fragments in
+    // registers and the DMA of K(j+2) and V(j+1) in flight:
+    //   S(j+1) = K(j+1) Q^T alongside the softmax of S(j);
+    //   wait for the DMA, barrier;
+    //   DMA K(j+3) over K(j+1) and V(j+2) over V(j), both last read before
+    //   this barrier;
+    //   read K(j+2) fragments, O += V(j)^T P(j) while they arrive, read V(j+1)
+    //   fragments.
+    template <int P>
+    __device__ __forceinline__ void iter(int j, int nk, int lim0, const half8* qf, half8* kf,
+                                         half8 (*vf)[NB], floatx16& s_cur, float& m, float& l,
+                                         floatx16* o) {
+        const floatx16 s_next = qk(kf, qf);
+        half8 pf[2];
+        softmax_block<false, NB, true>(s_cur, lim0 - j * G::BN, c, m, l, o, pf);
+        barrier_dma();
+        if (j + 3 < nk) dma(sl.k[P ^ 1], K, j + 3, true);
+        if (j + 2 < nk) dma(sl.v[P], V, j + 2, false);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + 2 < nk) read_k(kf, sl.k[P]);
+        pv(o, vf, pf);
+        read_v(vf, sl.v[P ^ 1]);
+        s_cur = s_next;
+    }
+
+    // Query tile qt over key tiles 0 .. nk-1.
+    __device__ void run(int qt, int nk) {
+        const int row = qt * G::BM + 32 * rg + n;
+        // last key this lane's row may see
+        const int vis = CAUSAL ? min(row, S - 1) : S - 1;
+        // the last key tile needs a mask: the diagonal (causal) or a ragged end
+        const bool mask_end = CAUSAL || (S % G::BN) != 0;
+
+        // prologue: K(0), V(0), K(1) into their slots; S(0); K(1) and V(0)
+        // fragments; then the DMA of K(2) and V(1)
+        dma(sl.k[0], K, 0, true);
+        dma(sl.v[0], V, 0, false);
+        if (nk > 1) dma(sl.k[1], K, 1, true);
+        half8 qf[D / 16];
+        {
+            const u32x4* src = reinterpret_cast<const u32x4*>(Q + base + (size_t)min(row, S - 1) * D);
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                u32x4 x = src[2 * kk + g];
+                x ^= qsign;
+                qf[kk] = __builtin_bit_cast(half8, x);
+            }
+        }
+        barrier_dma();
+        half8 kf[D / 16];
+        half8 vf[2][NB];
+        read_k(kf, sl.k[0]);
+        floatx16 s_cur = qk(kf, qf);
+        if (nk > 1) read_k(kf, sl.k[1]);
+        read_v(vf, sl.v[0]);
+        // every wave is done with K(0) before K(2) goes over it
+        barrier_dma();
+        if (nk > 2) dma(sl.k[0], K, 2, true);
+        if (nk > 1) dma(sl.v[1], V, 1, false);
+
+        float m = kNegInf, l = 0.f;
+        floatx16 o[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
+
+        const int lim0 = vis - (32 * kh + 4 * g);  // add -64 j for tile j
+        for (int j = 0; j + 1 < nk; j += 2) {
+            iter<0>(j, nk, lim0, qf, kf, vf, s_cur, m, l, o);
+            if (j + 2 < nk) iter<1>(j + 1, nk, lim0, qf, kf, vf, s_cur, m, l, o);
+        }
+        {
+            const int j = nk - 1;
+            half8 pf[2];
+            if (mask_end)
+                softmax_block<true, NB, false>(s_cur, lim0 - j * G::BN, c, m, l, o, pf);
+            else
+                softmax_block<false, NB, false>(s_cur, lim0 - j * G::BN, c, m, l, o, pf);
+            pv(o, vf, pf);
+        }
+
+        // merge the two key halves: each wave publishes the output blocks the
+        // other one writes (b % 2 != kh) and its (m, l) into its own tile
+        // array, then combines and writes its own blocks
+        barrier_dma();
+        _Float16* const arrs[4] = {sl.k[0], sl.k[1], sl.v[0], sl.v[1]};
+        float* mine = reinterpret_cast<float*>(arrs[2 * rg + kh]);
+        const float* theirs = reinterpret_cast<const float*>(arrs[2 * rg + (kh ^ 1)]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            if ((b & 1) != kh)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    reinterpret_cast<float4*>(mine)[((b >> 1) * 4 + q4) * 64 + lane] =
+                        float4{o[b][4 * q4], o[b][4 * q4 + 1], o[b][4 * q4 + 2], o[b][4 * q4 + 3]};
+        mine[16 * D + lane] = m;
+        mine[16 * D + 64 + lane] = l;
+        barrier_dma();
+        const float m1 = theirs[16 * D + lane], l1 = theirs[16 * D + 64 + lane];
+        const float mt = fmaxf(m, m1);  // finite: every row sees key 0 in the kh = 0 half
+        const float a0 = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m - mt);
+        const float a1 = m1 == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m1 - mt);
+        const float lt = sum_halves(l * a0 + l1 * a1);
+        const float inv = 1.0f / lt;
+        // register r of block b holds head dim 32b + 8(r/4) + 4g + r%4; lanes
+        // n and n+32 swap halves so that each lane stores 8 consecutive dims
+        // (16 bytes): lane g = 0 keeps dim group q4 = 2qq, g = 1 keeps 2qq+1
+        _Float16* orow = O + base + (size_t)min(row, S - 1) * D;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if ((b & 1) != kh) continue;
+            u32x2 x[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 p1 = reinterpret_cast<const float4*>(theirs)[((b >> 1) * 4 + q4) * 64 + lane];
+                const float x0 = (o[b][4 * q4] * a0 + p1.x * a1) * inv;
+                const float x1 = (o[b][4 * q4 + 1] * a0 + p1.y * a1) * inv;
+                const float x2 = (o[b][4 * q4 + 2] * a0 + p1.z * a1) * inv;
+                const float x3 = (o[b][4 * q4 + 3] * a0 + p1.w * a1) * inv;
+                x[q4][0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x0) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x1) << 16);
+                x[q4][1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x2) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x3) << 16);
+            }
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+                const u32x2 send = g ? x[2 * qq] : x[2 * qq + 1];
+                const u32x2 keep = g ? x[2 * qq + 1] : x[2 * qq];
+                u32x2 got;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) got[e] = (uint32_t)__shfl_xor((int)send[e], 32, 64);
+                const u32x4 v = g ? u32x4{got[0], got[1], keep[0], keep[1]}
+                                  : u32x4{keep[0], keep[1], got[0], got[1]};
+                if (row < S) *reinterpret_cast<u32x4*>(orow + 32 * b + 16 * qq + 8 * g) = v;
+            }
+        }
+        if (row < S) {
+            if (kh == 0 && g == 0) LSE[lse_base + row] = (mt + __builtin_amdgcn_logf(lt)) * kLn2;
+        }
+    }
+};
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 2)
+fwd_pipe_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
+                const _Float16* __restrict__ V, _Float16* __restrict__ O, float* __restrict__ LSE,
+                int BH, int S, float c, uint32_t qsign)
+{
+    using G = GeoP<D>;
+    __shared__ __attribute__((aligned(1024))) _Float16 k0[G::TILE];
+    __shared__ __attribute__((aligned(1024))) _Float16 k1[G::TILE];
+    __shared__ __attribute__((aligned(1024))) _Float16 v0[G::TILE];
+    __shared__ __attribute__((aligned(1024))) _Float16 v1[G::TILE];
+    const int T = (S + G::BM - 1) / G::BM;
+    const int bh = blockIdx.x % BH;
+    const int u = blockIdx.x / BH;
+    // causal: the first half of the grid runs the heavy tiles (last first),
+    // the second half the light ones (first first), so that workgroups
+    // launched half a grid apart carry complementary work
+    int qt = u;
+    if (CAUSAL) {
+        const int half = (T + 1) / 2;
+        qt = u < half ? T - 1 - u : u - half;
+    }
+    const int nk = CAUSAL ? qt + 1 : T;
+
+    Pipe<D, CAUSAL> f;
+    f.Q = Q;
+    f.K = K;
+    f.V = V;
+    f.O = O;
+    f.LSE = LSE;
+    f.sl.k[0] = k0;
+    f.sl.k[1] = k1;
+    f.sl.v[0] = v0;
+    f.sl.v[1] = v1;
+    f.S = S;
+    f.base = (size_t)bh * S * D;
+    f.lse_base = (size_t)bh * S;
+    f.c = c;
+    f.qsign = qsign;
+    f.tid = threadIdx.x;
+    f.lane = threadIdx.x & 63;
+    f.g = f.lane >> 5;
+    f.n = f.lane & 31;
+    f.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    f.rg = f.w & 1;
+    f.kh = f.w >> 1;
+    f.run(qt, nk);
+}
+
+}  // namespace
+
+hipError_t launch_fused_pipe_d64_d128(const FwdArgs& a) {
+    const int BH = a.B * a.H;
+    const int T = (a.S + 63) / 64;
+    const float c = fabsf(a.scale) * 1.44269504088896340736f;
+    const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
+    const dim3 grid((unsigned)((long long)BH * T));
+#define LAUNCH(DD, CC)                                                                          \
+    hipLaunchKernelGGL((fwd_pipe_kernel<DD, CC>), grid, dim3(256), 0, (hipStream_t)a.stream,   \
+                       (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,        \
+                       (_Float16*)a.o, a.lse, BH, a.S, c, qsign)
+    if (a.D == 64) {
+        if (a.causal) LAUNCH(64, true); else LAUNCH(64, false);
+    } else {
+        if (a.causal) LAUNCH(128, true); else LAUNCH(128, false);
+    }
+#undef LAUNCH
+    return hipGetLastError();
+}
+
+}  // namespace attn

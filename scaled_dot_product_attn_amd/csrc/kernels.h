@@ -16,9 +16,10 @@ struct FwdArgs {
     void* stream;
 };
 
-// Fused single-kernel forward, D = 64 or 128: two query tiles per workgroup
-// of eight waves (causal pairs t, T-1-t).
-hipError_t launch_fused_pair8_d64_d128(const FwdArgs& a);
+// Fused single-kernel forward, D = 64 or 128: one workgroup of four waves per
+// query tile, two per CU, K/V tiles loaded straight into LDS, the next tile's
+// Q K^T overlapped with the current tile's softmax.
+hipError_t launch_fused_pipe_d64_d128(const FwdArgs& a);
 // Fused single-kernel forward, D = 512 (head-dim halves summed in logit space).
 hipError_t launch_fused_d512(const FwdArgs& a);
 // Split-KV forward, D = 512: every query tile's key range cut into chunks of
