@@ -261,18 +261,26 @@ def main():
         n = w.B * w.H * w.S
         nbytes = 16 * n * w.D + 4 * n
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (mean_us * 1e-6) / 1e12
+    # the roofline takes the launch duration from the timed region (K launches
+    # back to back between two events on the launch stream); bracketing each
+    # call with its own events adds the launch latency to every call
+    step_us = ms_per_step * 1e3
+    achieved = flops / (step_us * 1e-6) / 1e12
     # the square D=128/512 causal shapes sit near the ridge; decode streams K/V
     bound_mfma = not decode and w.D >= 128 and w.causal
     if bound_mfma:
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_FP16_TFLOPS, "traffic": None}
     else:
-        gbs = nbytes / (mean_us * 1e-6) / 1e9
+        gbs = nbytes / (step_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": gbs / PEAK_HBM_GBS, "traffic": None}
     roof["traffic"] = measured_traffic(w.name, args.path)
-    roof["kernel_mean_us"] = mean_us
+    roof["launch_us"] = step_us
+    roof["launches_per_step"] = {"fused": 1, "unfused": 3, "splitkv": 2, "decode": 1 if not decode or
+                                 attn.decode_workspace_bytes(w.B, w.H, w.Sq, w.Sk, w.D, w.causal,
+                                                             dsplits) == 0 else 2,
+                                 "bwd": 2}[args.path]
     roof["per_launch"] = {"flops": flops, "alg_bytes": nbytes}
 
     out = {
