@@ -367,14 +367,20 @@ dec_merge_kernel(const float* __restrict__ ws, _Float16* __restrict__ O, float* 
     const int qt = rest / per_tile, rb = rest % per_tile;
     const int nch = ch.nchunks(qt);
     if (nch <= 1) return;
-    const float* slot0 = ws + ((size_t)bh * U + ch.first_unit(qt)) * G::SLOT;
     const int r = rb * 8 + (threadIdx.x >> 5);
     const int d0 = DPT * (threadIdx.x & 31);
     const int row = qt * G::BM + r;
+    // rows past Sq have no output (with a few query rows most of a tile)
+    if (row >= ch.Sq) return;
+    const float* slot0 = ws + ((size_t)bh * U + ch.first_unit(qt)) * G::SLOT;
+    // the chunks' loads are independent: batch them so that their latencies
+    // overlap instead of adding up
     float mt = kNegInf;
+#pragma unroll 8
     for (int cc = 0; cc < nch; ++cc) mt = fmaxf(mt, slot0[cc * G::SLOT + G::BM * D + r]);
     float lsum = 0.f;
     float acc[DPT] = {};
+#pragma unroll 4
     for (int cc = 0; cc < nch; ++cc) {
         const float* sl = slot0 + cc * G::SLOT;
         const float mc = sl[G::BM * D + r];
@@ -384,7 +390,6 @@ dec_merge_kernel(const float* __restrict__ ws, _Float16* __restrict__ O, float* 
 #pragma unroll
         for (int e = 0; e < DPT; ++e) acc[e] += wgt * sl[(size_t)r * D + d0 + e];
     }
-    if (row >= ch.Sq) return;
     const float inv = 1.0f / lsum;
     _Float16* orow = O + ((size_t)bh * ch.Sq + row) * D + d0;
 #pragma unroll
