@@ -41,6 +41,7 @@ METRIC = "attention fwd µs/call + effective TFLOP/s (% FP16 MFMA peak), 1 MI355
 # 4096 FLOP/clk/CU = 2516.6 TFLOP/s; HBM3E 8 TB/s.
 PEAK_FP16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
 PEAK_HBM_GBS = 8000.0
+SPIN_CYCLES = 2_000_000  # about 1 ms of GPU-side spin ahead of each suite round
 
 
 def parse():
@@ -61,6 +62,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=3.0,
                    help="minimum wall time of the oracle timing loop")
+    p.add_argument("--suite", action="store_true",
+                   help="time all five workloads in one process, interleaved round by round "
+                        "(warm and cold), plus the oracle at 1 thread and at all cores; prints "
+                        "one JSON line with a row per workload instead of the bench line")
+    p.add_argument("--rounds", type=int, default=300, help="suite: timed rounds")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of this many MiB (the reference "
                         "kernel for scaling HBM byte counters) and exit")
@@ -141,6 +147,120 @@ def measured_traffic(workload_name, path):
     return None
 
 
+def shader_clock_mhz():
+    """The current shader clock from sysfs (the line marked '*'), or None."""
+    import glob
+    for fn in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(fn):
+                if "*" in line:
+                    return int(line.split(":")[1].strip().rstrip("*").strip().lower()
+                               .replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
+def suite(args):
+    """All five workloads in one process, per the measurement protocol: 20
+    untimed calls per workload, then `rounds` rounds with the workloads
+    interleaved inside each round, every call bracketed by its own events on
+    the launch stream.  Two modes: warm (the same buffers every call) and cold
+    (12 rotating input sets, about 1.8 GB between two uses of one set, far
+    more than the 256 MB Infinity Cache).  Then the float64 oracle once per
+    workload at 1 thread and once at all threads, same inputs."""
+    import numpy as np
+    import torch
+    import scaled_dot_product_attn_amd as attn
+    from scaled_dot_product_attn_amd import inputs
+    dev = torch.device("cuda:0")
+    attn.load_library()
+    stream = torch.cuda.current_stream(dev)  # the stream attn.fwd launches on
+    ws = sorted(inputs.WORKLOADS.items())
+    nsets = 12
+    sets = {}
+    for c, w in ws:
+        sets[c] = []
+        for r in range(nsets):
+            qkv = w.qkv() if r == 0 else tuple(
+                inputs.normal_f16(w.seed_base + 100 * r + t, w.shape, w.sigma) for t in range(3))
+            sets[c].append(tuple(torch.from_numpy(x).to(dev) for x in qkv))
+    outs = {c: (torch.empty(w.shape, dtype=torch.float16, device=dev),
+                torch.empty(w.shape[:3], dtype=torch.float32, device=dev)) for c, w in ws}
+
+    def call(c, w, i):
+        q, k, v = sets[c][i]
+        o, lse = outs[c]
+        attn.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+    def timed(cold):
+        for c, w in ws:
+            for i in range(20):
+                call(c, w, i % nsets if cold else 0)
+        torch.cuda.synchronize(dev)
+        times = {c: [] for c, _ in ws}
+        for rnd in range(args.rounds):
+            # a GPU-side spin first, so that the host enqueues the whole round
+            # before the GPU reaches it: the events then bracket the kernels,
+            # not the host's launch latency
+            torch.cuda._sleep(SPIN_CYCLES)
+            evs = []
+            for c, w in ws:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                call(c, w, rnd % nsets if cold else 0)
+                b.record(stream)
+                evs.append((c, a, b))
+            if rnd == args.rounds // 2:
+                sclk.append(shader_clock_mhz())  # sampled while the round runs
+            torch.cuda.synchronize(dev)
+            for c, a, b in evs:
+                times[c].append(a.elapsed_time(b) * 1e3)
+        rows = []
+        for c, w in ws:
+            t = np.sort(np.array(times[c]))
+            med = float(np.median(t))
+            tf = w.flops() / med / 1e6
+            rows.append({"workload": w.name, "us_median": med,
+                         "us_p10": float(t[int(0.1 * (len(t) - 1))]),
+                         "us_p90": float(t[int(0.9 * (len(t) - 1))]),
+                         "tflops": tf, "pct_fp16_peak": 100 * tf / PEAK_FP16_TFLOPS,
+                         "alg_GBps": w.alg_bytes() / med / 1e3})
+        return rows
+
+    sclk = []
+    out = {"suite": "attention forward, five workloads interleaved per round",
+           "rounds": args.rounds, "timing": "events around each call, on the launch stream, "
+           "behind a GPU-side spin so that the round is enqueued before it runs"}
+    out["warm"] = timed(False)
+    out["cold"] = timed(True)
+    out["sclk_mhz_mid_round"] = sclk
+    print(json.dumps(out), flush=True)
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        allt = oracle.max_threads()
+        model = None
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
+        orc = {"cpu": model, "nproc": os.cpu_count(), "threads_all": allt, "rows": []}
+        for c, w in ws:
+            q, k, v = w.qkv()
+            rec = {"workload": w.name}
+            for nt in (1, allt):
+                t0 = time.perf_counter()
+                oracle.attn_fwd(q, k, v, w.causal, w.scale, nthreads=nt)
+                rec[f"seconds_{nt}_threads"] = time.perf_counter() - t0
+            orc["rows"].append(rec)
+            print(json.dumps({"oracle_row": rec}), flush=True)
+        out["oracle"] = orc
+        print(json.dumps(out), flush=True)
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -149,6 +269,9 @@ def main():
               "figure is not measured here.", file=sys.stderr)
         sys.exit(2)
 
+    if args.suite:
+        suite(args)
+        return
     import torch
     if args.copy_calibration:
         n = args.copy_calibration << 20

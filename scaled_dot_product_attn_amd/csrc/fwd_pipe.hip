@@ -194,6 +194,14 @@ struct Pipe {
     // This wave writes PIECES 1 KB pieces; lane L of a piece lands at byte
     // 16 L of it, i.e. row ROWS_PER_PIECE * piece + L / CPR at physical chunk
     // L % CPR, so it loads the logical chunk that the swizzle puts there.
+    //
+    // The load is written as inline assembly (M0 = LDS address of the piece)
+    // rather than the compiler builtin: for the builtin the compiler cannot
+    // tell that a later transposed LDS read of another slot does not alias the
+    // load's destination, and waits for every load in flight before that
+    // read, i.e. for the tiles just issued.  Here the only waits are the
+    // explicit ones in barrier_dma(), which every reader of a slot passes
+    // after the load into that slot.
     __device__ __forceinline__ void dma(_Float16* slot, const _Float16* t, int j, bool isk) const {
         const auto r = tile_rsrc(t, j * G::BN);
 #pragma unroll
@@ -202,8 +210,12 @@ struct Pipe {
             const int row = G::ROWS_PER_PIECE * piece + lane / G::CPR;
             const int phys = lane % G::CPR;
             const int logical = phys ^ (isk ? swz_k<D>(row) : swz_vp<D>(row));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (LdsPtr)(slot + piece * 512), 16, (row * D + 8 * logical) * 2, 0, 0, 0);
+            const uint32_t m0 = (uint32_t)(uintptr_t)(LdsPtr)(slot + piece * 512);
+            // s_nop: one wait state between the M0 write and its use
+            asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :
+                         : "v"((row * D + 8 * logical) * 2), "s"(r), "{m0}"(m0)
+                         : "memory");
         }
     }
     // K fragments of keys 32kh .. +31 (A operand of S^T = K Q^T)
@@ -350,9 +362,13 @@ struct Pipe {
         // other one writes (b % 2 != kh) and its (m, l) into its own tile
         // array, then combines and writes its own blocks
         barrier_dma();
-        _Float16* const arrs[4] = {sl.k[0], sl.k[1], sl.v[0], sl.v[1]};
-        float* mine = reinterpret_cast<float*>(arrs[2 * rg + kh]);
-        const float* theirs = reinterpret_cast<const float*>(arrs[2 * rg + (kh ^ 1)]);
+        // wave (rg, kh) owns tile array 2 rg + kh (selected, not indexed, so
+        // that no pointer table goes to scratch memory)
+        auto arr = [&](int i) -> _Float16* {
+            return i == 0 ? sl.k[0] : i == 1 ? sl.k[1] : i == 2 ? sl.v[0] : sl.v[1];
+        };
+        float* mine = reinterpret_cast<float*>(arr(2 * rg + kh));
+        const float* theirs = reinterpret_cast<const float*>(arr(2 * rg + (kh ^ 1)));
 #pragma unroll
         for (int b = 0; b < NB; ++b)
             if ((b & 1) != kh)
