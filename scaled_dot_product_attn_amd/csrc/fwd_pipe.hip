@@ -190,10 +190,11 @@ struct Pipe {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(t + base + (size_t)j0 * D),
                                                  (short)0, min(S - j0, G::BN) * D * 2, 0x00020000);
     }
-    // Tile j of t straight into an LDS slot (global -> LDS, no registers).
-    // This wave writes PIECES 1 KB pieces; lane L of a piece lands at byte
-    // 16 L of it, i.e. row ROWS_PER_PIECE * piece + L / CPR at physical chunk
-    // L % CPR, so it loads the logical chunk that the swizzle puts there.
+    // One 1 KB piece (u < PIECES) of this wave's share of a tile, from the
+    // buffer r straight into an LDS slot (global -> LDS, no registers).  Lane
+    // L of a piece lands at byte 16 L of it, i.e. row ROWS_PER_PIECE * piece
+    // + L / CPR at physical chunk L % CPR, so it loads the logical chunk that
+    // the swizzle puts there.
     //
     // The load is written as inline assembly (M0 = LDS address of the piece)
     // rather than the compiler builtin: for the builtin the compiler cannot
@@ -202,21 +203,24 @@ struct Pipe {
     // read, i.e. for the tiles just issued.  Here the only waits are the
     // explicit ones in barrier_dma(), which every reader of a slot passes
     // after the load into that slot.
+    __device__ __forceinline__ void dma_piece(_Float16* slot, const __amdgpu_buffer_rsrc_t r,
+                                              int u, bool isk) const {
+        const int piece = w * G::PIECES + u;
+        const int row = G::ROWS_PER_PIECE * piece + lane / G::CPR;
+        const int phys = lane % G::CPR;
+        const int logical = phys ^ (isk ? swz_k<D>(row) : swz_vp<D>(row));
+        const uint32_t m0 = (uint32_t)(uintptr_t)(LdsPtr)(slot + piece * 512);
+        // s_nop: one wait state between the M0 write and its use
+        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"((row * D + 8 * logical) * 2), "s"(r), "{m0}"(m0)
+                     : "memory");
+    }
+    // Tile j of t, this wave's pieces.
     __device__ __forceinline__ void dma(_Float16* slot, const _Float16* t, int j, bool isk) const {
         const auto r = tile_rsrc(t, j * G::BN);
 #pragma unroll
-        for (int u = 0; u < G::PIECES; ++u) {
-            const int piece = w * G::PIECES + u;
-            const int row = G::ROWS_PER_PIECE * piece + lane / G::CPR;
-            const int phys = lane % G::CPR;
-            const int logical = phys ^ (isk ? swz_k<D>(row) : swz_vp<D>(row));
-            const uint32_t m0 = (uint32_t)(uintptr_t)(LdsPtr)(slot + piece * 512);
-            // s_nop: one wait state between the M0 write and its use
-            asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                         :
-                         : "v"((row * D + 8 * logical) * 2), "s"(r), "{m0}"(m0)
-                         : "memory");
-        }
+        for (int u = 0; u < G::PIECES; ++u) dma_piece(slot, r, u, isk);
     }
     // K fragments of keys 32kh .. +31 (A operand of S^T = K Q^T)
     __device__ __forceinline__ void read_k(half8* kf, const _Float16* slot) const {
@@ -280,10 +284,12 @@ struct Pipe {
     // registers and the DMA of K(j+2) and V(j+1) in flight:
     //   S(j+1) = K(j+1) Q^T alongside the softmax of S(j);
     //   wait for the DMA, barrier;
-    //   DMA K(j+3) over K(j+1) and V(j+2) over V(j), both last read before
-    //   this barrier;
-    //   read K(j+2) fragments, O += V(j)^T P(j) while they arrive, read V(j+1)
-    //   fragments.
+    //   O += V(j)^T P(j), each matrix instruction followed by one 1 KB load
+    //   (K(j+3) over K(j+1), then V(j+2) over V(j), both slots last read
+    //   before this barrier) and one K(j+2) fragment read: a wave stalls on
+    //   issuing a load while the texture unit drains the other waves' loads,
+    //   and this way the matrix core works through those stalls;
+    //   read the V(j+1) fragments.
     template <int P>
     __device__ __forceinline__ void iter(int j, int nk, int lim0, const half8* qf, half8* kf,
                                          half8 (*vf)[NB], floatx16& s_cur, float& m, float& l,
@@ -292,11 +298,31 @@ struct Pipe {
         half8 pf[2];
         softmax_block<false, NB, true>(s_cur, lim0 - j * G::BN, c, m, l, o, pf);
         barrier_dma();
-        if (j + 3 < nk) dma(sl.k[P ^ 1], K, j + 3, true);
-        if (j + 2 < nk) dma(sl.v[P], V, j + 2, false);
-        __builtin_amdgcn_sched_barrier(0);
-        if (j + 2 < nk) read_k(kf, sl.k[P]);
-        pv(o, vf, pf);
+        // O += V(j)^T P(j), one matrix instruction at a time, each followed
+        // by one 1 KB tile load (K(j+3), then V(j+2)) and one K(j+2)
+        // fragment read, so that the loads queue at the texture unit while
+        // the matrix core runs
+        {
+            const bool dk = j + 3 < nk, dv = j + 2 < nk;
+            const auto rk = tile_rsrc(K, (j + 3) * G::BN);
+            const auto rv = tile_rsrc(V, (j + 2) * G::BN);
+            const int krow = 32 * kh + n;
+            const _Float16* kp = sl.k[P] + krow * D;
+            const int ksw = swz_k<D>(krow);
+            static_assert(2 * NB == 2 * G::PIECES && 2 * NB == D / 16, "one load and one read per MFMA");
+#pragma unroll
+            for (int i = 0; i < 2 * NB; ++i) {
+                const int h = i / NB, b = i % NB;
+                o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[h][b], pf[h], o[b], 0, 0, 0);
+                if (i < G::PIECES) {
+                    if (dk) dma_piece(sl.k[P ^ 1], rk, i, true);
+                } else {
+                    if (dv) dma_piece(sl.v[P], rv, i - G::PIECES, false);
+                }
+                if (dv) kf[i] = *reinterpret_cast<const half8*>(kp + 8 * ((2 * i + g) ^ ksw));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
         read_v(vf, sl.v[P ^ 1]);
         s_cur = s_next;
     }
