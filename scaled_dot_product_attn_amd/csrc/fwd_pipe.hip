@@ -89,12 +89,19 @@ __device__ __forceinline__ int swz_vp(int r) {
 // o: the output blocks.  P^T (fp16, round to nearest even) goes to pf as the
 // B operand of the two 16-key P V steps.
 //
-// The weights are formed against the current reference max before the row
-// max is known; only when the row max outgrows the reference by more than
-// 2^kLazyTau are the output and sum rescaled and the weights formed again.
-// Max and sum run as trees (short dependence chains), and the speculative
-// weights are pinned ahead of the branch so that they stay in the same
-// scheduling region as the next tile's matrix instructions.
+// The weights are formed against the current reference max m without
+// looking at the row max.  Every weight is at most the lane's sum of them, so
+// while every lane's sum stays within 2^kLazyTau no weight exceeds it and
+// nothing else is done; otherwise (or when the sum is NaN: m = -inf meeting a
+// masked key) the row max is taken, the reference moves to it, the output and
+// sum are rescaled and the weights formed again.  So the row-max tree runs
+// only on the rare blocks that move the reference, and every weight stays
+// <= 2^kLazyTau (fp16-safe) either way.  The sum runs as a tree (short
+// dependence chains), and the speculative weights are pinned ahead of the
+// branch so that they stay in the same scheduling region as the next tile's
+// matrix instructions.
+constexpr float kLazyBound = 256.0f;  // 2^kLazyTau
+static_assert(kLazyTau == 8.0f, "kLazyBound = 2^kLazyTau");
 template <bool MASK, int NB, bool PIPE>
 __device__ __forceinline__ void softmax_block(floatx16 s, int lim, float c, float& m, float& l,
                                               floatx16* o, half8* pf) {
@@ -103,10 +110,6 @@ __device__ __forceinline__ void softmax_block(floatx16 s, int lim, float c, floa
         for (int r = 0; r < 16; ++r)
             if ((8 * (r >> 2) + (r & 3)) > lim) s[r] = kNegInf;
     }
-    const float mx = fmaxf(fmaxf(fmaxf(fmaxf(s[0], s[1]), s[2]), fmaxf(fmaxf(s[3], s[4]), s[5])),
-                           fmaxf(fmaxf(fmaxf(s[6], s[7]), s[8]),
-                                 fmaxf(fmaxf(fmaxf(s[9], s[10]), s[11]),
-                                       fmaxf(fmaxf(fmaxf(s[12], s[13]), s[14]), s[15]))));
     // weights against reference mref: P^T in fp16 into pf, and this lane's
     // sum in fp32 (four partial sums, then a tree)
     auto weights = [&](float mref) {
@@ -130,7 +133,6 @@ __device__ __forceinline__ void softmax_block(floatx16 s, int lim, float c, floa
         asm volatile("" : "+v"(x));
         pf[h] = __builtin_bit_cast(half8, x);
     }
-    const float mxh = max_halves(mx);
     if (PIPE) {
         // interleave the next tile's Q K^T (8 MFMAs, issued by the caller in
         // this region) with this softmax's vector work
@@ -141,10 +143,16 @@ __device__ __forceinline__ void softmax_block(floatx16 s, int lim, float c, floa
             __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
         }
     }
-    // fmaxf keeps the candidate finite when every key is masked (c * -inf)
-    // or c == 0 (0 * -inf)
-    const float cand = fmaxf(c * mxh, -kFltMax);
-    if (__builtin_amdgcn_ballot_w64(cand > m + kLazyTau) != 0) {
+    // every weight is at most the lane's sum; the sum is NaN when m = -inf
+    // meets a masked key (-inf + inf), and that too takes the branch
+    if (__builtin_amdgcn_ballot_w64(!(psum <= kLazyBound)) != 0) {
+        const float mx = fmaxf(fmaxf(fmaxf(fmaxf(s[0], s[1]), s[2]), fmaxf(fmaxf(s[3], s[4]), s[5])),
+                               fmaxf(fmaxf(fmaxf(s[6], s[7]), s[8]),
+                                     fmaxf(fmaxf(fmaxf(s[9], s[10]), s[11]),
+                                           fmaxf(fmaxf(fmaxf(s[12], s[13]), s[14]), s[15]))));
+        // fmaxf keeps the candidate finite when every key is masked
+        // (c * -inf) or c == 0 (0 * -inf)
+        const float cand = fmaxf(c * max_halves(mx), -kFltMax);
         const float m_new = fmaxf(m, cand);
         const float alpha = __builtin_amdgcn_exp2f(m - m_new);
         m = m_new;
@@ -412,8 +420,9 @@ struct Pipe {
         const float lt = sum_halves(l * a0 + l1 * a1);
         const float inv = 1.0f / lt;
         // register r of block b holds head dim 32b + 8(r/4) + 4g + r%4; lanes
-        // n and n+32 swap halves so that each lane stores 8 consecutive dims
-        // (16 bytes): lane g = 0 keeps dim group q4 = 2qq, g = 1 keeps 2qq+1
+        // n and n+32 swap halves (v_permlane32_swap, no LDS round trip) so
+        // that each lane stores 8 consecutive dims (16 bytes): lane g = 0
+        // keeps dim group q4 = 2qq, g = 1 keeps 2qq+1
         _Float16* orow = O + base + (size_t)min(row, S - 1) * D;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -433,13 +442,15 @@ struct Pipe {
             }
 #pragma unroll
             for (int qq = 0; qq < 2; ++qq) {
-                const u32x2 send = g ? x[2 * qq] : x[2 * qq + 1];
-                const u32x2 keep = g ? x[2 * qq + 1] : x[2 * qq];
-                u32x2 got;
-#pragma unroll
-                for (int e = 0; e < 2; ++e) got[e] = (uint32_t)__shfl_xor((int)send[e], 32, 64);
-                const u32x4 v = g ? u32x4{got[0], got[1], keep[0], keep[1]}
-                                  : u32x4{keep[0], keep[1], got[0], got[1]};
+                // swap the upper half-wave's x[2qq] with the lower half-wave's
+                // x[2qq+1]: afterwards the first result holds dims 8g .. 8g+3
+                // and the second dims 8g+4 .. 8g+7 of this lane's 16-byte
+                // group, in both halves
+                const auto s0 = __builtin_amdgcn_permlane32_swap(x[2 * qq][0], x[2 * qq + 1][0],
+                                                                 false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(x[2 * qq][1], x[2 * qq + 1][1],
+                                                                 false, false);
+                const u32x4 v = u32x4{s0[0], s1[0], s0[1], s1[1]};
                 if (row < S) *reinterpret_cast<u32x4*>(orow + 32 * b + 16 * qq + 8 * g) = v;
             }
         }

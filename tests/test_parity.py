@@ -99,6 +99,50 @@ def test_batch_heads_layout(gpu, oracle_mod, D):
         check(o, lse, o_ref, l_ref, f"B3 H5 S77 D{D} causal={causal}")
 
 
+# ---------------------------------- grids of more than one wave of workgroups
+
+# More 64-row query tiles than 2 x 256 (two workgroups on each of the 256
+# CUs), so that workgroups start as others finish.  Cases: one tile per head,
+# odd tile counts, B*H a multiple of 8 and not, both head dims, both masks,
+# ragged S.
+MULTIWAVE = [
+    (1, 520, 64, 64, False),
+    (1, 520, 64, 128, True),
+    (3, 7, 1590, 64, False),
+    (2, 16, 1030, 128, True),
+    (1, 24, 1400, 64, True),
+    (1, 40, 900, 128, False),
+]
+
+
+@pytest.mark.parametrize("B,H,S,D,causal", MULTIWAVE)
+def test_multiwave_grids(gpu, oracle_mod, B, H, S, D, causal):
+    assert B * H * ((S + 63) // 64) > 512
+    shape = (B, H, S, D)
+    seed = 12_000 + S + D + H
+    q, k, v = (rnd(seed + t, shape) for t in range(3))
+    sc = 1 / math.sqrt(D)
+    log(f"multi-wave B={B} H={H} S={S} D={D} causal={causal}")
+    o, lse = run(gpu, q, k, v, causal, sc)
+    # heads are independent: the oracle checks a sample of (batch, head) pairs
+    picks = sorted({(0, 0), (B - 1, H - 1), (B // 2, H // 2), (0, H - 1), (B - 1, 0)})
+    if S <= 64:
+        picks = [(b, h) for b in range(B) for h in range(H)]
+    for b, h in picks:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        o_ref, l_ref = oracle_mod.attn_fwd(q[sl], k[sl], v[sl], causal, sc)
+        check(o[sl], lse[sl], o_ref, l_ref, f"multi-wave {shape} causal={causal} b={b} h={h}")
+
+
+def test_multiwave_repeat_bit_identical(gpu):
+    shape = (2, 16, 1030, 128)
+    q, k, v = (rnd(12_500 + t, shape) for t in range(3))
+    o1, l1 = run(gpu, q, k, v, True, 0.088)
+    o2, l2 = run(gpu, q, k, v, True, 0.088)
+    assert inputs.sha256(o1) == inputs.sha256(o2)
+    assert inputs.sha256(l1) == inputs.sha256(l2)
+
+
 # ------------------------------------------------------------------ the pins
 
 @pytest.mark.parametrize("S", [64, 128])
