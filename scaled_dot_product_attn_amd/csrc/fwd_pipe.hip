@@ -29,6 +29,9 @@
 // O += V(j)^T P(j) while they arrive, and reads the V(j+1) fragments.  No
 // LDS latency sits between the barrier and the next matrix instruction.
 //
+// The Q tile comes in the same way (through the second V slot, before V(1)
+// needs it) and then stays in registers as the B operand of Q K^T.
+//
 // The K slots are XOR-swizzled by row (no padding, so that a 1 KB load
 // lands as whole rows), the V slots as for the transposed reads.
 //
@@ -343,30 +346,44 @@ struct Pipe {
         // the last key tile needs a mask: the diagonal (causal) or a ragged end
         const bool mask_end = CAUSAL || (S % G::BN) != 0;
 
-        // prologue: K(0), V(0), K(1) into their slots; S(0); K(1) and V(0)
-        // fragments; then the DMA of K(2) and V(1)
+        // prologue: K(0), Q, V(0), K(1) into their slots (Q through v[1],
+        // free until V(1) is loaded, laid out like a K tile: sixteen 1 KB
+        // loads instead of each lane gathering its row 16 bytes at a time);
+        // wait for K(0) and Q only (the last 2 or 1 tiles' loads may still
+        // be in flight), S(0); then wait for the rest, K(1) and V(0)
+        // fragments, and the DMA of K(2) and V(1)
         dma(sl.k[0], K, 0, true);
+        dma(sl.v[1], Q, qt, true);
         dma(sl.v[0], V, 0, false);
         if (nk > 1) dma(sl.k[1], K, 1, true);
         half8 qf[D / 16];
+        if (nk > 1) {
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(2 * G::PIECES) : "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(G::PIECES) : "memory");
+        }
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
         {
-            const u32x4* src = reinterpret_cast<const u32x4*>(Q + base + (size_t)min(row, S - 1) * D);
+            const int qrow = 32 * rg + n;
+            const _Float16* qp = sl.v[1] + qrow * D;
+            const int sw = swz_k<D>(qrow);
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
-                u32x4 x = src[2 * kk + g];
+                u32x4 x = *reinterpret_cast<const u32x4*>(qp + 8 * ((2 * kk + g) ^ sw));
                 x ^= qsign;
                 qf[kk] = __builtin_bit_cast(half8, x);
             }
         }
-        barrier_dma();
         half8 kf[D / 16];
         half8 vf[2][NB];
         read_k(kf, sl.k[0]);
         floatx16 s_cur = qk(kf, qf);
+        // V(0) and K(1) landed everywhere; every wave is done with K(0) and Q
+        // before K(2) and V(1) go over them
+        barrier_dma();
         if (nk > 1) read_k(kf, sl.k[1]);
         read_v(vf, sl.v[0]);
-        // every wave is done with K(0) before K(2) goes over it
-        barrier_dma();
         if (nk > 2) dma(sl.k[0], K, 2, true);
         if (nk > 1) dma(sl.v[1], V, 1, false);
 
