@@ -5,18 +5,20 @@ A step is one attn_fwd call: the whole fused path (load, Q K^T, mask, online
 softmax, P V, normalise, store) over one batch of synthetic inputs already
 resident in HBM.  Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload C] [--rotate R]
+    python bench.py [--steps K] [--warmup W] [--workload C] [--rotate R] [--eager]
+    python bench.py --suite            # all five workloads, warm and cold
 
 Timing protocol (after "An Optimal Mapper Meets a Real GPU", section
 "Experiment one": CUDA-event timing over many interleaved reps on an
 exclusively held GPU, and the cold-start lesson of arXiv 2609.33916 section
 2.3: one process, untimed warmup first):
   * W untimed warm-up calls;
-  * the timed region: synchronize, then K back-to-back calls between two
-    events, synchronize -> ms_per_step and the throughput `value`;
+  * the timed region: the K calls captured once into a HIP graph and replayed
+    (untimed once, then between two events on the launch stream, with a
+    synchronize on both sides) -> ms_per_step, the throughput `value` and the
+    roofline's launch duration; --eager times K host launches instead;
   * a second pass brackets every call with its own pair of HIP events on the
-    launch stream -> per-call median/p10/p90 and the mean kernel duration used
-    for the roofline fraction.
+    launch stream -> per-call median/p10/p90 (host launch latency included).
 With --rotate R the calls cycle through R independent input sets (R*inputs
 larger than the 256 MB Infinity Cache gives HBM-cold inputs); the default
 R = 1 re-reads the same buffers, so inputs are largely cache-resident.
@@ -60,6 +62,8 @@ def parse():
     p.add_argument("--splits", type=int, default=3,
                    help="split-KV path: chunks of the longest key range (D = 512 only)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--eager", action="store_true",
+                   help="time the K steps as K host launches instead of one HIP graph replay")
     p.add_argument("--cpu-seconds", type=float, default=3.0,
                    help="minimum wall time of the oracle timing loop")
     p.add_argument("--suite", action="store_true",
@@ -349,18 +353,35 @@ def main():
         step(i)
     torch.cuda.synchronize(dev)
 
-    # timed region: K back-to-back steps
+    # timed region: K back-to-back steps.  By default the K steps are captured
+    # once into a HIP graph (every buffer is allocated above; the C ABI
+    # launches on torch's current stream, which is the capture stream inside
+    # the capture) and the graph is replayed, untimed once, then timed: the
+    # same K launches without K host round trips in between.
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize(dev)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     t_wall = time.perf_counter()
     start.record(stream)
-    for i in range(args.steps):
-        step(i)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i)
     end.record(stream)
     torch.cuda.synchronize(dev)
     t_wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
+    if graph is not None:
+        del graph
 
     # per-call events on the launch stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -426,7 +447,9 @@ def main():
                    "path": args.path, "input_sets": args.rotate,
                    **({"splits": args.splits} if args.path == "splitkv" else {}),
                    "cache": "warm (same buffers)" if args.rotate == 1 else
-                            f"rotating {args.rotate} input sets"},
+                            f"rotating {args.rotate} input sets",
+                   "launch": "eager, one host launch per step" if args.eager else
+                             "one HIP graph of the K steps, replayed"},
         "us_per_call": {"mean": mean_us, "median": med_us, "p10": p10, "p90": p90,
                         "back_to_back": ms_per_step * 1e3},
         "pct_fp16_peak": 100 * value / PEAK_FP16_TFLOPS,
