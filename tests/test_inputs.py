@@ -110,3 +110,32 @@ def test_sigma_scaling_is_exact_before_rounding():
     z = inputs.normal_f64(9, 1000)
     x = inputs.normal_f16(9, (1000,), sigma=0.5)
     assert np.array_equal(x, (0.5 * z).astype(np.float16))
+
+
+def _golden_hashes():
+    out = {}
+    for row in _read_golden("input_sha256.txt"):
+        name, t, shape, h = row.split()
+        out[(name, t)] = (tuple(int(x) for x in shape.split("x")), h)
+    return out
+
+
+@pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
+def test_workload_input_bytes_are_pinned(c):
+    """The generator reproduces the recorded SHA-256 of every input tensor
+    (the two 1 GB decode caches are recorded too; they take long enough to
+    generate that the CPU suite leaves them out)."""
+    want = _golden_hashes()
+    w = inputs.WORKLOADS[c]
+    for t, x in zip("QKV", w.qkv()):
+        shape, h = want[(w.name, t)]
+        assert x.shape == shape and x.dtype == np.float16
+        assert inputs.sha256(x) == h, f"{w.name} {t}"
+
+
+def test_decode_input_bytes_are_pinned():
+    want = _golden_hashes()
+    w = inputs.DECODE_WORKLOADS[1]
+    for t, x in zip("QKV", w.qkv()):
+        shape, h = want[(w.name, t)]
+        assert x.shape == shape and inputs.sha256(x) == h, f"{w.name} {t}"
