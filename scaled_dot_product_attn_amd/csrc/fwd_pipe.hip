@@ -268,6 +268,21 @@ struct Pipe {
             }
         }
     }
+    // One V^T fragment vf[h][b] (keys 32kh + 16h .. +15, head dims 32b .. +31).
+    __device__ __forceinline__ half8 read_v1(const _Float16* slot, int h, int b) const {
+        const int n16 = n >> 4, jj = n & 15;
+        const int sub = (jj & 3) >> 1, half = (jj & 1);
+        const int sw = swz_vp<D>(jj >> 2);
+        const _Float16* pb = slot + (32 * kh + 4 * g + (jj >> 2)) * D + 4 * half +
+                             8 * ((4 * b + 2 * n16 + sub) ^ sw);
+        half4 part[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            part[t] = __builtin_bit_cast(
+                half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_half4*)(pb + (16 * h + 8 * t) * D)));
+        return half8{part[0][0], part[0][1], part[0][2], part[0][3],
+                     part[1][0], part[1][1], part[1][2], part[1][3]};
+    }
     __device__ __forceinline__ floatx16 qk(const half8* kf, const half8* qf) const {
         floatx16 acc;
 #pragma unroll
@@ -297,10 +312,11 @@ struct Pipe {
     //   wait for the DMA, barrier;
     //   O += V(j)^T P(j), each matrix instruction followed by one 1 KB load
     //   (K(j+3) over K(j+1), then V(j+2) over V(j), both slots last read
-    //   before this barrier) and one K(j+2) fragment read: a wave stalls on
-    //   issuing a load while the texture unit drains the other waves' loads,
-    //   and this way the matrix core works through those stalls;
-    //   read the V(j+1) fragments.
+    //   before this barrier), one K(j+2) fragment read and the read of the
+    //   V(j+1) fragment into the registers that instruction consumed: a wave
+    //   stalls on issuing a load while the texture unit drains the other
+    //   waves' loads, and this way the matrix core works through those
+    //   stalls and the LDS reads issue under them.
     template <int P>
     __device__ __forceinline__ void iter(int j, int nk, int lim0, const half8* qf, half8* kf,
                                          half8 (*vf)[NB], floatx16& s_cur, float& m, float& l,
@@ -331,10 +347,11 @@ struct Pipe {
                     if (dv) dma_piece(sl.v[P], rv, i - G::PIECES, false);
                 }
                 if (dv) kf[i] = *reinterpret_cast<const half8*>(kp + 8 * ((2 * i + g) ^ ksw));
+                // the fragment this MFMA consumed, now of V(j+1)
+                vf[h][b] = read_v1(sl.v[P ^ 1], h, b);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        read_v(vf, sl.v[P ^ 1]);
         s_cur = s_next;
     }
 
