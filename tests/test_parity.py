@@ -260,6 +260,39 @@ def test_slice_consistency(gpu):
             assert np.array_equal(o[1:2, 2:3], o1) and np.array_equal(lse[1:2, 2:3], l1)
 
 
+def test_linearity_in_v_and_key_permutation(gpu):
+    """P13 on the GPU: O is linear in V for fixed Q, K (the probabilities do
+    not depend on V), and permuting the key/value rows jointly leaves a
+    non-causal result unchanged; both within the parity tolerance (the GPU
+    rounds P and O to fp16, and the sums run in a different order)."""
+    for D in (64, 128, 512):
+        shape = (1, 2, 190, D)
+        q, k = (rnd(19_500 + D + t, shape) for t in range(2))
+        # V1 and V2 on the grid 2^-8 within [-4, 4], so that V1 + V2 (grid 2^-8
+        # within [-8, 8], 11 significant bits) is exact in fp16
+        def grid(seed):
+            x = rnd(seed, shape).astype(np.float64)
+            return np.clip(np.round(x * 256) / 256, -4, 4).astype(np.float16)
+        v1, v2 = grid(19_600 + D), grid(19_700 + D)
+        v12 = (v1.astype(np.float32) + v2.astype(np.float32)).astype(np.float16)
+        assert np.array_equal(v12.astype(np.float32), v1.astype(np.float32) + v2.astype(np.float32))
+        sc = 1 / math.sqrt(D)
+        for causal in (False, True):
+            o1, l1 = run(gpu, q, k, v1, causal, sc)
+            o2, l2 = run(gpu, q, k, v2, causal, sc)
+            o12, l12 = run(gpu, q, k, v12, causal, sc)
+            lhs = o12.astype(np.float64)
+            rhs = o1.astype(np.float64) + o2.astype(np.float64)
+            assert np.all(np.abs(lhs - rhs) <= O_TOL + O_TOL * np.abs(rhs)), f"linearity D={D}"
+            # the log-sum-exp does not see V at all
+            assert np.array_equal(l1, l2) and np.array_equal(l1, l12)
+        perm = np.random.default_rng(19_800 + D).permutation(shape[2])
+        o, l = run(gpu, q, k, v1, False, sc)
+        op, lp = run(gpu, q, k[:, :, perm], v1[:, :, perm], False, sc)
+        assert np.all(np.abs(op.astype(np.float64) - o) <= O_TOL + O_TOL * np.abs(o))
+        assert np.all(np.abs(lp.astype(np.float64) - l) <= LSE_TOL * np.maximum(1, np.abs(l)))
+
+
 def test_large_logits(gpu, oracle_mod):
     """P12: scale = 8/sqrt(D) (logit spreads of tens): finite and in parity."""
     for D in (64, 128, 512):
