@@ -24,9 +24,10 @@
 // each a separate LDS array.  Iteration j starts with the K(j+1) and V(j)
 // fragments in registers and the loads of K(j+2) and V(j+1) in flight;
 // after S(j+1) and the softmax of S(j) every wave waits for its loads and
-// meets the barrier, then issues the loads of K(j+3) over K(j+1) and V(j+2)
-// over V(j) (both read before the barrier), reads the K(j+2) fragments, runs
-// O += V(j)^T P(j) while they arrive, and reads the V(j+1) fragments.  No
+// meets the barrier, then runs O += V(j)^T P(j) one matrix instruction at a
+// time, each followed by one 1 KB load (K(j+3) over K(j+1), then V(j+2)
+// over V(j), both read before the barrier), one K(j+2) fragment read and
+// the V(j+1) fragment that replaces the one the instruction consumed.  No
 // LDS latency sits between the barrier and the next matrix instruction.
 //
 // The Q tile comes in the same way (through the second V slot, before V(1)
@@ -326,9 +327,9 @@ struct Pipe {
         softmax_block<false, NB, true>(s_cur, lim0 - j * G::BN, c, m, l, o, pf);
         barrier_dma();
         // O += V(j)^T P(j), one matrix instruction at a time, each followed
-        // by one 1 KB tile load (K(j+3), then V(j+2)) and one K(j+2)
-        // fragment read, so that the loads queue at the texture unit while
-        // the matrix core runs
+        // by one 1 KB tile load (K(j+3), then V(j+2)), one K(j+2) fragment
+        // read and one V(j+1) fragment, so that the loads queue at the
+        // texture unit while the matrix core runs
         {
             const bool dk = j + 3 < nk, dv = j + 2 < nk;
             const auto rk = tile_rsrc(K, (j + 3) * G::BN);
