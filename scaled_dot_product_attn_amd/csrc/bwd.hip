@@ -80,9 +80,13 @@ struct Bwd {
     uint32_t qsign;         // 0x80008000 when the scale is negative
 
     // Buffer over rows r0 .. r0+63 of t, clipped at S: reads past it return zero.
+    // The size goes through readfirstlane: computed as a clamp it otherwise
+    // lands in a vector register, the descriptor counts as divergent and the
+    // compiler wraps every load in a loop over its distinct values.
     __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const _Float16* t, int r0) const {
+        const int bytes = __builtin_amdgcn_readfirstlane(min(max(S - r0, 0), 64) * D * 2);
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(t + base + (size_t)r0 * D),
-                                                 (short)0, min(max(S - r0, 0), 64) * D * 2, 0x00020000);
+                                                 (short)0, bytes, 0x00020000);
     }
     // Rows r0 .. r0+63 of t (past S read as zero) -> registers x[CH].
     __device__ __forceinline__ void load(u32x4* x, const _Float16* t, int r0) const {
