@@ -211,14 +211,16 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     u32x4 xq[G::CH], xo[G::CH];
     float lv = 0.f, dv_ = 0.f;
     auto stage_of = [&](int s) { return lds + s * STAGE; };
+    // The row values are loaded first and used only in put(): consumed
+    // right after the tile loads, they made the wave wait for those too.
     auto fetch = [&](int qt) {
-        f.load(xq, Q, qt * 64);
-        f.load(xo, dO, qt * 64);
         if (f.tid < 64) {
             const int row = qt * 64 + f.tid;
-            lv = row < S ? LSE[f.row_base + row] * kLog2e : 0.f;
+            lv = row < S ? LSE[f.row_base + row] : 0.f;
             dv_ = row < S ? dlt[f.row_base + row] : 0.f;
         }
+        f.load(xq, Q, qt * 64);
+        f.load(xo, dO, qt * 64);
     };
     auto put = [&](int s) {
         _Float16* st = stage_of(s);
@@ -226,7 +228,7 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
         f.store(st + G::TILE, xo);
         if (f.tid < 64) {
             float* fl = reinterpret_cast<float*>(st + 2 * G::TILE);
-            fl[f.tid] = lv;
+            fl[f.tid] = lv * kLog2e;
             fl[64 + f.tid] = dv_;
         }
     };
