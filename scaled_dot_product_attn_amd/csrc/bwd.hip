@@ -139,6 +139,45 @@ struct Bwd {
                                 part[1][0], part[1][1], part[1][2], part[1][3]};
             }
     }
+    // Output tile in LDS: 64 rows of D halfs, padded by 16 bytes per row.
+    static constexpr int OP = D + 8;
+    // Accumulator block acc (register r: row r0 + 8(r/4) + 4g + r%4, column
+    // 32b + n) rounded to fp16 into the output tile.
+    __device__ __forceinline__ void to_tile(_Float16* ot, const floatx16& acc, int r0, int b,
+                                            float mul) const {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            ot[(r0 + 8 * (r >> 2) + 4 * g + (r & 3)) * OP + 32 * b + n] = (_Float16)(acc[r] * mul);
+    }
+    // Rows r0 .. r0+63 of the output tile -> t (rows past S are not written):
+    // every lane stores whole 16-byte chunks of a row.
+    __device__ __forceinline__ void from_tile(_Float16* t, const _Float16* ot, int r0) const {
+#pragma unroll
+        for (int u = 0; u < G::CH; ++u) {
+            const int ci = tid + G::NT * u;
+            const int row = ci / G::CPR, cc = ci % G::CPR;
+            if (r0 + row < S)
+                *reinterpret_cast<u32x4*>(t + base + (size_t)(r0 + row) * D + 8 * cc) =
+                    *reinterpret_cast<const u32x4*>(ot + row * OP + 8 * cc);
+        }
+    }
+    // Partial accumulator blocks through LDS, one float4 per lane and slot.
+    __device__ __forceinline__ void give(float4* buf, const floatx16& acc, int slot) const {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            buf[(4 * slot + q4) * 64 + lane] =
+                float4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
+    }
+    __device__ __forceinline__ void take(floatx16& acc, const float4* buf, int slot) const {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 x = buf[(4 * slot + q4) * 64 + lane];
+            acc[4 * q4] += x.x;
+            acc[4 * q4 + 1] += x.y;
+            acc[4 * q4 + 2] += x.z;
+            acc[4 * q4 + 3] += x.w;
+        }
+    }
     // Fragment of rows (r0 + n) straight from global memory (rows past S read
     // as zero); xsign flips fp16 signs.
     __device__ __forceinline__ void grows(half8* f, const _Float16* t, int r0, uint32_t xsign) const {
@@ -269,15 +308,26 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
         }
         const int key = k0 + 32 * lo + n;
         half8 pa[2], sa[2];
+        // only the diagonal tile and tiles that reach past S need the mask
+        const bool edge = (CAUSAL && qt == kt) || qt * 64 + 64 > S || k0 + 64 > S;
+        if (edge) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int qrow = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const float lse_r = l4[r >> 2][r & 3], dlt_r = d4[r >> 2][r & 3];
-            const bool vis = qrow < S && key < S && (!CAUSAL || key <= qrow);
-            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -lse_r)) : 0.f;
-            const float ds = p * (dp[r] - dlt_r);
-            pa[r >> 3][r & 7] = (_Float16)p;
-            sa[r >> 3][r & 7] = (_Float16)ds;
+            for (int r = 0; r < 16; ++r) {
+                const int qrow = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
+                const float lse_r = l4[r >> 2][r & 3], dlt_r = d4[r >> 2][r & 3];
+                const bool vis = qrow < S && key < S && (!CAUSAL || key <= qrow);
+                const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -lse_r)) : 0.f;
+                pa[r >> 3][r & 7] = (_Float16)p;
+                sa[r >> 3][r & 7] = (_Float16)(p * (dp[r] - dlt_r));
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float lse_r = l4[r >> 2][r & 3], dlt_r = d4[r >> 2][r & 3];
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -lse_r));
+                pa[r >> 3][r & 7] = (_Float16)p;
+                sa[r >> 3][r & 7] = (_Float16)(p * (dp[r] - dlt_r));
+            }
         }
         half8 bf[2][NB];
         f.cols(bf, Os, 32 * hi);
@@ -296,41 +346,46 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
         s ^= 1;
     }
 
-    // the two query halves (hi = 0, 1) hold partial sums over disjoint rows:
-    // hi = 1 publishes, hi = 0 adds in a fixed order and writes
+    // The two query halves (hi = 0, 1) hold partial sums over disjoint rows.
+    // Wave (lo, 0) finishes dK of keys 32lo .. +31 and wave (lo, 1) their dV,
+    // each adding the other's partial (a + b, the same in either order); the
+    // fp16 results go through LDS so that every global store is a 16-byte
+    // chunk of a row.  Register r of block b: key k0 + 32lo + 8(r/4) + 4g + r%4,
+    // head dim 32b + n.
     barrier();
-    float4* buf = reinterpret_cast<float4*>(lds) + lo * (2 * NB * 4) * 64;
-    if (hi == 1) {
+    {
+        float4* mine = reinterpret_cast<float4*>(lds) + (2 * lo + hi) * (NB * 4) * 64;
+        if (hi == 0) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+            for (int b = 0; b < NB; ++b) f.give(mine, dv[b], b);
+        } else {
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                buf[(4 * b + q4) * 64 + lane] =
-                    float4{dk[b][4 * q4], dk[b][4 * q4 + 1], dk[b][4 * q4 + 2], dk[b][4 * q4 + 3]};
-                buf[(4 * (NB + b) + q4) * 64 + lane] =
-                    float4{dv[b][4 * q4], dv[b][4 * q4 + 1], dv[b][4 * q4 + 2], dv[b][4 * q4 + 3]};
-            }
+            for (int b = 0; b < NB; ++b) f.give(mine, dk[b], b);
+        }
     }
     barrier();
-    if (hi == 1) return;
-    // register r of block b: key k0 + 32lo + 8(r/4) + 4g + r%4, head dim 32b + n
+    {
+        const float4* other = reinterpret_cast<const float4*>(lds) + (2 * lo + (hi ^ 1)) * (NB * 4) * 64;
+        if (hi == 0) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+            for (int b = 0; b < NB; ++b) f.take(dk[b], other, b);
+        } else {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 pk = buf[(4 * b + q4) * 64 + lane];
-            const float4 pv = buf[(4 * (NB + b) + q4) * 64 + lane];
-            const float sk[4] = {pk.x, pk.y, pk.z, pk.w}, sv[4] = {pv.x, pv.y, pv.z, pv.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int key = k0 + 32 * lo + 8 * q4 + 4 * g + e;
-                if (key < S) {
-                    const size_t at = f.base + (size_t)key * D + 32 * b + n;
-                    dK[at] = (_Float16)((dk[b][4 * q4 + e] + sk[e]) * scale);
-                    dV[at] = (_Float16)(dv[b][4 * q4 + e] + sv[e]);
-                }
-            }
+            for (int b = 0; b < NB; ++b) f.take(dv[b], other, b);
         }
+    }
+    barrier();
+    _Float16* ot = lds + hi * (64 * Bwd<D>::OP);  // hi = 0: dK tile, 1: dV tile
+    if (hi == 0) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) f.to_tile(ot, dk[b], 32 * lo, b, scale);
+    } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) f.to_tile(ot, dv[b], 32 * lo, b, 1.f);
+    }
+    barrier();
+    f.from_tile(dK, lds, k0);
+    f.from_tile(dV, lds + 64 * Bwd<D>::OP, k0);
 }
 
 // dQ for one 64-row query tile.  Wave (lo, hi): query rows 32lo .. +31 of the
@@ -431,14 +486,24 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
         for (int kk = 0; kk < D / 16; ++kk)
             dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk], ob[kk], dp, 0, 0, 0);
 
-        // register r holds key k0 + 8(r/4) + 4g + r%4 for this lane's query
+        // register r holds key k0 + 8(r/4) + 4g + r%4 for this lane's query;
+        // only the diagonal tile and tiles that reach past S need the mask
         half8 sa[2];
+        const bool edge = (CAUSAL && kt == qt) || qt * 64 + 64 > S || kt * 64 + 64 > S;
+        if (edge) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool vis = qrow < S && key < S && (!CAUSAL || key <= qrow);
-            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -lse_q)) : 0.f;
-            sa[r >> 3][r & 7] = (_Float16)(p * (dp[r] - dlt_q));
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + 8 * (r >> 2) + 4 * g + (r & 3);
+                const bool vis = qrow < S && key < S && (!CAUSAL || key <= qrow);
+                const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -lse_q)) : 0.f;
+                sa[r >> 3][r & 7] = (_Float16)(p * (dp[r] - dlt_q));
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -lse_q));
+                sa[r >> 3][r & 7] = (_Float16)(p * (dp[r] - dlt_q));
+            }
         }
         half8 bf[2][NB];
         f.cols(bf, Ks, 32 * hi);
@@ -454,33 +519,37 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
         s ^= 1;
     }
 
-    // the two key halves (hi = 0, 1) hold partial sums over disjoint keys
+    // The two key halves (hi = 0, 1) hold partial sums over disjoint keys.
+    // Wave (lo, hi) finishes head-dim blocks hi*NB/2 .. of queries 32lo .. +31,
+    // adding the other's partial (a + b, the same in either order); the fp16
+    // results go through LDS so that every global store is a 16-byte chunk of
+    // a row.  Register r of block b: query qt*64 + 32lo + 8(r/4) + 4g + r%4,
+    // head dim 32b + n.
+    constexpr int HB = NB / 2;
     barrier();
-    float4* buf = reinterpret_cast<float4*>(lds) + lo * (NB * 4) * 64;
-    if (hi == 1) {
+    float4* mine = reinterpret_cast<float4*>(lds) + (2 * lo + hi) * (HB * 4) * 64;
+    const float4* other = reinterpret_cast<const float4*>(lds) + (2 * lo + (hi ^ 1)) * (HB * 4) * 64;
+    if (hi == 0) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < HB; ++b) f.give(mine, dq[HB + b], b);
+        barrier();
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                buf[(4 * b + q4) * 64 + lane] =
-                    float4{dq[b][4 * q4], dq[b][4 * q4 + 1], dq[b][4 * q4 + 2], dq[b][4 * q4 + 3]};
+        for (int b = 0; b < HB; ++b) f.take(dq[b], other, b);
+        barrier();
+#pragma unroll
+        for (int b = 0; b < HB; ++b) f.to_tile(lds, dq[b], 32 * lo, b, scale);
+    } else {
+#pragma unroll
+        for (int b = 0; b < HB; ++b) f.give(mine, dq[b], b);
+        barrier();
+#pragma unroll
+        for (int b = 0; b < HB; ++b) f.take(dq[HB + b], other, b);
+        barrier();
+#pragma unroll
+        for (int b = 0; b < HB; ++b) f.to_tile(lds, dq[HB + b], 32 * lo, HB + b, scale);
     }
     barrier();
-    if (hi == 1) return;
-    // register r of block b: query qt*64 + 32lo + 8(r/4) + 4g + r%4, head dim 32b + n
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 pq = buf[(4 * b + q4) * 64 + lane];
-            const float sq[4] = {pq.x, pq.y, pq.z, pq.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = qt * 64 + 32 * lo + 8 * q4 + 4 * g + e;
-                if (row < S)
-                    dQ[f.base + (size_t)row * D + 32 * b + n] = (_Float16)((dq[b][4 * q4 + e] + sq[e]) * scale);
-            }
-        }
+    f.from_tile(dQ, lds, qt * 64);
 }
 
 template <int D, bool CAUSAL>
