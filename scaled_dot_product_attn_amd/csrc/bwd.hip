@@ -178,6 +178,11 @@ struct Bwd {
             acc[4 * q4 + 3] += x.w;
         }
     }
+    __device__ __forceinline__ void flip(half8* f, uint32_t xsign) const {
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            f[kk] = __builtin_bit_cast(half8, __builtin_bit_cast(u32x4, f[kk]) ^ xsign);
+    }
     // Fragment of rows (r0 + n) straight from global memory (rows past S read
     // as zero); xsign flips fp16 signs.
     __device__ __forceinline__ void grows(half8* f, const _Float16* t, int r0, uint32_t xsign) const {
@@ -232,11 +237,6 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     f.qsign = qsign;
     const int lo = f.lo, hi = f.hi, g = f.g, n = f.n, lane = f.lane;
 
-    // this wave's K and V rows as B operands (k = head dim), kept for the whole walk
-    half8 kb[D / 16], vb[D / 16];
-    f.grows(kb, K, k0 + 32 * lo, qsign);  // a negative scale negates the logits
-    f.grows(vb, V, k0 + 32 * lo, 0u);
-
     floatx16 dk[NB], dv[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -271,8 +271,15 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
             fl[64 + f.tid] = dv_;
         }
     };
+    // All start-up loads are issued before the first wait: the first query
+    // tile, then this wave's K and V rows (B operands with k = head dim, kept
+    // for the whole walk).  A negative scale negates the logits through K.
     fetch(qt0);
+    half8 kb[D / 16], vb[D / 16];
+    f.grows(kb, K, k0 + 32 * lo, 0u);
+    f.grows(vb, V, k0 + 32 * lo, 0u);
     put(0);
+    f.flip(kb, qsign);
     int s = 0;
     for (int qt = qt0; qt < T; ++qt) {
         barrier();  // query tile qt is in stage s; every wave is done with qt-1
@@ -426,11 +433,18 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     f.qsign = qsign;
     const int lo = f.lo, hi = f.hi, g = f.g, n = f.n, lane = f.lane;
 
+    // All start-up loads are issued before the first wait: this lane's LSE,
+    // the first key tile, then this wave's Q, dO and O rows.
     const int qrow = qt * 64 + 32 * lo + n;  // the query this lane owns
+    // (the row is clamped rather than the load made conditional: a select
+    // right after the load would wait for it)
+    const float lse_raw = LSE[f.row_base + min(qrow, S - 1)];
+    u32x4 xk[G::CH], xv[G::CH];
+    f.load(xk, K, 0);
+    f.load(xv, V, 0);
     half8 qb[D / 16], ob[D / 16];
-    f.grows(qb, Q, qt * 64 + 32 * lo, qsign);
+    f.grows(qb, Q, qt * 64 + 32 * lo, 0u);
     f.grows(ob, dO, qt * 64 + 32 * lo, 0u);
-    const float lse_q = qrow < S ? LSE[f.row_base + qrow] * kLog2e : 0.f;
     // Dlt = dO . O of this lane's query: each half of the wave holds half of
     // the head dims (8g .. 8g+7 of every 16)
     float dlt_q;
@@ -453,9 +467,8 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
         for (int r = 0; r < 16; ++r) dq[b][r] = 0.f;
 
     const int nT = CAUSAL ? qt + 1 : T;
-    u32x4 xk[G::CH], xv[G::CH];
-    f.load(xk, K, 0);
-    f.load(xv, V, 0);
+    f.flip(qb, qsign);  // a negative scale negates the logits through Q
+    const float lse_q = qrow < S ? lse_raw * kLog2e : 0.f;
     f.store(lds, xk);
     f.store(lds + G::TILE, xv);
     int s = 0;
