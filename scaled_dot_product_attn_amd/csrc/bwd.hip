@@ -290,29 +290,33 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
         const float* fl = reinterpret_cast<const float*>(Qs + 2 * G::TILE);
         const int q0 = qt * 64 + 32 * hi;  // first query row of this wave
 
-        half8 af[D / 16];
-        f.rows(af, Qs, 32 * hi);
-        floatx16 sacc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk], kb[kk], sacc, 0, 0, 0);
-        f.rows(af, Os, 32 * hi);
-        floatx16 dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dp[r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk], vb[kk], dp, 0, 0, 0);
-
-        // register r holds query q0 + 8(r/4) + 4g + r%4 for key k0 + 32lo + n
+        // Every LDS read of the products is issued before the first of them,
+        // the row values first: with one wave per SIMD nothing else hides
+        // their latency.  Register r of a score block holds query
+        // q0 + 8(r/4) + 4g + r%4 for key k0 + 32lo + n.
         float4 l4[4], d4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             l4[j] = *reinterpret_cast<const float4*>(fl + 32 * hi + 8 * j + 4 * g);
             d4[j] = *reinterpret_cast<const float4*>(fl + 64 + 32 * hi + 8 * j + 4 * g);
         }
+        half8 aq[D / 16], ao[D / 16];
+        f.rows(aq, Qs, 32 * hi);
+        f.rows(ao, Os, 32 * hi);
+        __builtin_amdgcn_sched_barrier(0);
+        floatx16 sacc, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = dp[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(aq[kk], kb[kk], sacc, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(ao[kk], vb[kk], dp, 0, 0, 0);
+        }
+        // the dO columns of dV += P^T dO go out while the scores are formed,
+        // the Q columns of dK += dS^T Q before the dV products
+        half8 bo[2][NB], bq[2][NB];
+        f.cols(bo, Os, 32 * hi);
+        __builtin_amdgcn_sched_barrier(0);
         const int key = k0 + 32 * lo + n;
         half8 pa[2], sa[2];
         // only the diagonal tile and tiles that reach past S need the mask
@@ -336,19 +340,18 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                 sa[r >> 3][r & 7] = (_Float16)(p * (dp[r] - dlt_r));
             }
         }
-        half8 bf[2][NB];
-        f.cols(bf, Os, 32 * hi);
+        f.cols(bq, Qs, 32 * hi);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                dv[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[h], bf[h][b], dv[b], 0, 0, 0);
-        f.cols(bf, Qs, 32 * hi);
+                dv[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[h], bo[h][b], dv[b], 0, 0, 0);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                dk[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[h], bf[h][b], dk[b], 0, 0, 0);
+                dk[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[h], bq[h][b], dk[b], 0, 0, 0);
         if (more) put(s ^ 1);
         s ^= 1;
     }
@@ -483,21 +486,24 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
         const _Float16* Vs = Ks + G::TILE;
         const int k0 = kt * 64 + 32 * hi;  // first key of this wave
 
-        half8 af[D / 16];
-        f.rows(af, Ks, 32 * hi);
-        floatx16 sacc;
+        // Every LDS read of the products is issued ahead of its use: with
+        // one wave per SIMD nothing else hides their latency.  The K columns
+        // of dQ += dS K go out while the scores are formed.
+        half8 ak[D / 16], av[D / 16];
+        f.rows(ak, Ks, 32 * hi);
+        f.rows(av, Vs, 32 * hi);
+        __builtin_amdgcn_sched_barrier(0);
+        floatx16 sacc, dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+        for (int r = 0; r < 16; ++r) sacc[r] = dp[r] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk], qb[kk], sacc, 0, 0, 0);
-        f.rows(af, Vs, 32 * hi);
-        floatx16 dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dp[r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk], ob[kk], dp, 0, 0, 0);
+        for (int kk = 0; kk < D / 16; ++kk) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak[kk], qb[kk], sacc, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk], ob[kk], dp, 0, 0, 0);
+        }
+        half8 bf[2][NB];
+        f.cols(bf, Ks, 32 * hi);
+        __builtin_amdgcn_sched_barrier(0);
 
         // register r holds key k0 + 8(r/4) + 4g + r%4 for this lane's query;
         // only the diagonal tile and tiles that reach past S need the mask
@@ -518,8 +524,6 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                 sa[r >> 3][r & 7] = (_Float16)(p * (dp[r] - dlt_q));
             }
         }
-        half8 bf[2][NB];
-        f.cols(bf, Ks, 32 * hi);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
