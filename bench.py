@@ -38,6 +38,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd µs/call + effective TFLOP/s (% FP16 MFMA peak), 1 MI355X"
+# --path bwd times the backward (dQ, dK, dV), so its line carries its own name
+METRIC_BWD = "attention bwd µs/call + effective TFLOP/s of the five products (% FP16 MFMA peak), 1 MI355X"
 
 # MI355X published peaks (dense): FP16 MFMA 2.5 PFLOP/s, here 256 CU x 2.4 GHz x
 # 4096 FLOP/clk/CU = 2516.6 TFLOP/s; HBM3E 8 TB/s.
@@ -438,7 +440,7 @@ def main():
     roof["per_launch"] = {"flops": flops, "alg_bytes": nbytes}
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if args.path == "bwd" else METRIC,
         "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
