@@ -141,26 +141,30 @@ struct Bwd {
                                 part[1][0], part[1][1], part[1][2], part[1][3]};
             }
     }
-    // Output tile in LDS: 64 rows of D halfs, padded by 16 bytes per row.
-    static constexpr int OP = D + 8;
-    // Accumulator block acc (register r: row r0 + 8(r/4) + 4g + r%4, column
-    // 32b + n) rounded to fp16 into the output tile.
-    __device__ __forceinline__ void to_tile(_Float16* ot, const floatx16& acc, int r0, int b,
-                                            float mul) const {
+    // Output block b of row `row` (this lane's row: the accumulators are
+    // transposed, register r holding head dim 32b + 8(r/4) + 4g + r%4), times
+    // mul and rounded to fp16, stored as two 16-byte chunks: lanes n and n+32
+    // swap halves (v_permlane32_swap, no LDS round trip) so that each holds 8
+    // consecutive dims.  Rows past S are not written.
+    __device__ __forceinline__ void store_block(_Float16* t, const floatx16& acc, int row, int b,
+                                                float mul) const {
+        uint32_t x[4][2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            ot[(r0 + 8 * (r >> 2) + 4 * g + (r & 3)) * OP + 32 * b + n] = (_Float16)(acc[r] * mul);
-    }
-    // Rows r0 .. r0+63 of the output tile -> t (rows past S are not written):
-    // every lane stores whole 16-byte chunks of a row.
-    __device__ __forceinline__ void from_tile(_Float16* t, const _Float16* ot, int r0) const {
+        for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
-        for (int u = 0; u < G::CH; ++u) {
-            const int ci = tid + G::NT * u;
-            const int row = ci / G::CPR, cc = ci % G::CPR;
-            if (r0 + row < S)
-                *reinterpret_cast<u32x4*>(t + base + (size_t)(r0 + row) * D + 8 * cc) =
-                    *reinterpret_cast<const u32x4*>(ot + row * OP + 8 * cc);
+            for (int e = 0; e < 2; ++e)
+                x[q4][e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(acc[4 * q4 + 2 * e] * mul)) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(acc[4 * q4 + 2 * e + 1] * mul)) << 16);
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+            // the upper half-wave's x[2qq] trades places with the lower
+            // half-wave's x[2qq+1]: afterwards lane g holds dims
+            // 16qq + 8g .. +7 of the block
+            const auto s0 = __builtin_amdgcn_permlane32_swap(x[2 * qq][0], x[2 * qq + 1][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(x[2 * qq][1], x[2 * qq + 1][1], false, false);
+            const u32x4 v = u32x4{s0[0], s1[0], s0[1], s1[1]};
+            if (row < S)
+                *reinterpret_cast<u32x4*>(t + base + (size_t)row * D + 32 * b + 16 * qq + 8 * g) = v;
         }
     }
     // Partial accumulator blocks through LDS, one float4 per lane and slot.

@@ -11,8 +11,10 @@ using namespace detail;
 // query rows 32hi .. +31 of every query tile that sees the keys.
 //   S  = Q K^T  : A = Q rows (LDS), B = this wave's K rows (registers)
 //   dP = dO V^T : A = dO rows (LDS), B = this wave's V rows (registers)
-//   dV += P^T dO, dK += dS^T Q : A = P^T / dS^T (score registers), B = dO / Q
-//                 columns (transposed LDS reads)
+//   dV^T += dO^T P, dK^T += Q^T dS : A = dO / Q columns (transposed LDS
+//                 reads), B = P / dS (score registers); the accumulators hold
+//                 lane = key, registers = head dims, so that rows are stored
+//                 from registers
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 1)
 bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
@@ -156,22 +158,21 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                dv[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[h], bo[h][b], dv[b], 0, 0, 0);
+                dv[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bo[h][b], pa[h], dv[b], 0, 0, 0);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                dk[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[h], bq[h][b], dk[b], 0, 0, 0);
+                dk[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bq[h][b], sa[h], dk[b], 0, 0, 0);
         if (more) put(s ^ 1);
         s ^= 1;
     }
 
     // The two query halves (hi = 0, 1) hold partial sums over disjoint rows.
     // Wave (lo, 0) finishes dK of keys 32lo .. +31 and wave (lo, 1) their dV,
-    // each adding the other's partial (a + b, the same in either order); the
-    // fp16 results go through LDS so that every global store is a 16-byte
-    // chunk of a row.  Register r of block b: key k0 + 32lo + 8(r/4) + 4g + r%4,
-    // head dim 32b + n.
+    // each adding the other's partial (a + b, the same in either order), and
+    // stores its rows from registers.  Register r of block b: head dim
+    // 32b + 8(r/4) + 4g + r%4 of key k0 + 32lo + n.
     barrier();
     {
         float4* mine = reinterpret_cast<float4*>(lds) + (2 * lo + hi) * (NB * 4) * 64;
@@ -194,18 +195,14 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
             for (int b = 0; b < NB; ++b) f.take(dv[b], other, b);
         }
     }
-    barrier();
-    _Float16* ot = lds + hi * (64 * Bwd<D>::OP);  // hi = 0: dK tile, 1: dV tile
+    const int key = k0 + 32 * lo + n;
     if (hi == 0) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) f.to_tile(ot, dk[b], 32 * lo, b, scale);
+        for (int b = 0; b < NB; ++b) f.store_block(dK, dk[b], key, b, scale);
     } else {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) f.to_tile(ot, dv[b], 32 * lo, b, 1.f);
+        for (int b = 0; b < NB; ++b) f.store_block(dV, dv[b], key, b, 1.f);
     }
-    barrier();
-    f.from_tile(dK, lds, k0);
-    f.from_tile(dV, lds + 64 * Bwd<D>::OP, k0);
 }
 
 template <int D, bool CAUSAL>

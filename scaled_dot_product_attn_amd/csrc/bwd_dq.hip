@@ -14,8 +14,10 @@ using namespace detail;
 // tile, keys 32hi .. +31 of every key tile the rows see.
 //   S^T  = K Q^T  : A = K rows (LDS), B = this wave's Q rows (registers)
 //   dP^T = V dO^T : A = V rows (LDS), B = this wave's dO rows (registers)
-//   dQ  += dS K   : A = dS (score registers: lane = query, registers = keys),
-//                   B = K columns (transposed LDS reads)
+//   dQ^T += K^T dS^T : A = K columns (transposed LDS reads), B = dS (score
+//                   registers: lane = query, registers = keys); the
+//                   accumulator holds lane = query, registers = head dims, so
+//                   that rows are stored from registers
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 1)
 bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
@@ -140,7 +142,7 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                dq[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[h], bf[h][b], dq[b], 0, 0, 0);
+                dq[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[h][b], sa[h], dq[b], 0, 0, 0);
         if (more) {
             f.store(lds + (s ^ 1) * STAGE, xk);
             f.store(lds + (s ^ 1) * STAGE + G::TILE, xv);
@@ -150,10 +152,9 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
 
     // The two key halves (hi = 0, 1) hold partial sums over disjoint keys.
     // Wave (lo, hi) finishes head-dim blocks hi*NB/2 .. of queries 32lo .. +31,
-    // adding the other's partial (a + b, the same in either order); the fp16
-    // results go through LDS so that every global store is a 16-byte chunk of
-    // a row.  Register r of block b: query qt*64 + 32lo + 8(r/4) + 4g + r%4,
-    // head dim 32b + n.
+    // adding the other's partial (a + b, the same in either order), and stores
+    // those blocks of its rows from registers.  Register r of block b: head dim
+    // 32b + 8(r/4) + 4g + r%4 of query qt*64 + 32lo + n.
     constexpr int HB = NB / 2;
     barrier();
     float4* mine = reinterpret_cast<float4*>(lds) + (2 * lo + hi) * (HB * 4) * 64;
@@ -164,21 +165,17 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
         barrier();
 #pragma unroll
         for (int b = 0; b < HB; ++b) f.take(dq[b], other, b);
-        barrier();
 #pragma unroll
-        for (int b = 0; b < HB; ++b) f.to_tile(lds, dq[b], 32 * lo, b, scale);
+        for (int b = 0; b < HB; ++b) f.store_block(dQ, dq[b], qrow, b, scale);
     } else {
 #pragma unroll
         for (int b = 0; b < HB; ++b) f.give(mine, dq[b], b);
         barrier();
 #pragma unroll
         for (int b = 0; b < HB; ++b) f.take(dq[HB + b], other, b);
-        barrier();
 #pragma unroll
-        for (int b = 0; b < HB; ++b) f.to_tile(lds, dq[HB + b], 32 * lo, HB + b, scale);
+        for (int b = 0; b < HB; ++b) f.store_block(dQ, dq[HB + b], qrow, HB + b, scale);
     }
-    barrier();
-    f.from_tile(dQ, lds, qt * 64);
 }
 
 template <int D, bool CAUSAL>
