@@ -66,3 +66,47 @@ def test_graph_replays_match_eager(gpu, path):
         # eager work between replays
         call(0)
         torch.cuda.synchronize()
+
+
+def test_graph_backward_replays_match_eager(gpu):
+    """The backward (two launches sharing a workspace) captured over several
+    input sets and replayed: every replay gives the eager dQ, dK, dV bit for
+    bit, with eager calls and synchronisations in between."""
+    import torch
+    B, H, S, D, causal, sc = 2, 3, 300, 128, True, 0.088
+    sets = []
+    for i, (q, k, v) in enumerate(_inputs(92_000, (B, H, S, D), 3)):
+        do = torch.from_numpy(inputs.normal_f16(92_500 + i, (B, H, S, D))).cuda()
+        o, lse = gpu.fwd(q, k, v, causal=causal, scale=sc)
+        sets.append((q, k, v, o, lse, do))
+    torch.cuda.synchronize()
+    ws = torch.empty(gpu.bwd_workspace_bytes(B, H, S), dtype=torch.uint8, device="cuda")
+    grads = [tuple(torch.empty((B, H, S, D), dtype=torch.float16, device="cuda") for _ in range(3))
+             for _ in sets]
+
+    def call(i):
+        q, k, v, o, lse, do = sets[i]
+        dq, dk, dv = grads[i]
+        gpu.bwd(q, k, v, o, lse, do, causal=causal, scale=sc, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for i in range(len(sets)):
+        call(i)
+    torch.cuda.synchronize()
+    eager = [tuple(t.clone() for t in g3) for g3 in grads]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(len(sets)):
+            call(i)
+    for rep in range(4):
+        for g3 in grads:
+            for t in g3:
+                t.fill_(float("nan"))
+        ws.fill_(0xFF)  # a stale workspace must not leak into the result
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for g3, e3 in zip(grads, eager):
+            for name, t, e in zip(("dQ", "dK", "dV"), g3, e3):
+                assert torch.equal(t, e), f"backward: {name} differs on replay {rep}"
+        call(1)
+        torch.cuda.synchronize()
