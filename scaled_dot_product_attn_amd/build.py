@@ -36,6 +36,9 @@ PER_FILE = {
     # MFMA accumulators in ordinary VGPRs: otherwise the compiler copies the
     # loop-carried dQ blocks to AGPRs and back in every iteration.
     "bwd_dq.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"],
+    # the same for the D = 512 kernel: its online-softmax rescale of the O
+    # accumulator otherwise runs on AGPR copies
+    "fwd_d512.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"],
 }
 
 
