@@ -19,7 +19,7 @@ using namespace detail;
 //                   accumulator holds lane = query, registers = head dims, so
 //                   that rows are stored from registers
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, 2)
 bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
               const _Float16* __restrict__ V, const _Float16* __restrict__ dO,
               const _Float16* __restrict__ O, const float* __restrict__ LSE,
@@ -29,11 +29,19 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     using G = GeoB<D>;
     constexpr int NB = G::NB;
     constexpr int STAGE = 2 * G::TILE;  // K tile, V tile
+    constexpr int PIECES = G::TILE * 2 / 1024 / G::NW;  // 1 KB pieces of a tile per wave
+    constexpr int RPP = 1024 / (2 * D);                 // rows per piece
     __shared__ __attribute__((aligned(1024))) _Float16 lds[2 * STAGE];
+    using LdsPtr = __attribute__((address_space(3))) void*;
 
     const int T = (S + 63) / 64;
     const int bh = blockIdx.x % BH;
-    const int qt = CAUSAL ? T - 1 - blockIdx.x / BH : blockIdx.x / BH;  // heaviest first
+    // Causal: the first half of the grid takes the heavy query tiles
+    // (T-1, T-2, ...), the second half the light ones (0, 1, ...).  With two
+    // workgroups per CU, workgroup i and i + grid/2 share a CU when the grid
+    // fills the chip once, and carry T+1 key tiles between them.
+    const int j = blockIdx.x / BH;
+    const int qt = CAUSAL ? (j < T / 2 ? T - 1 - j : j - T / 2) : j;
 
     Bwd<D> f;
     f.S = S;
@@ -50,15 +58,38 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     f.qsign = qsign;
     const int lo = f.lo, hi = f.hi, g = f.g, n = f.n, lane = f.lane;
 
+    // Piece u (< PIECES) of this wave's share of rows r0 .. r0+63 of t into
+    // the swizzled tile dst, straight from global memory into LDS (no staging
+    // registers).  Lane L of a 1 KB piece lands at byte 16 L of it (row
+    // RPP piece + L / CPR, physical chunk L % CPR), so it loads the logical
+    // chunk the swizzle puts there; rows past S read as zero.  Inline
+    // assembly with M0 = the LDS address, as the forward's tile loads, so the
+    // only waits on these loads are the explicit ones before each barrier.
+    auto dma_piece = [&](_Float16* dst, const _Float16* t, int r0, int u) {
+        const int piece = w * PIECES + u;
+        const int row = RPP * piece + lane / G::CPR;
+        const int logical = (lane % G::CPR) ^ swz_b<D>(row);
+        const auto r = f.rsrc(t, r0);
+        const uint32_t m0 = (uint32_t)(uintptr_t)(LdsPtr)(dst + piece * 512);
+        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"((row * D + 8 * logical) * 2), "s"(r), "{m0}"(m0)
+                     : "memory");
+    };
+    auto dma_tile = [&](int st, int kt) {
+#pragma unroll
+        for (int u = 0; u < PIECES; ++u) dma_piece(lds + st * STAGE, K, kt * 64, u);
+#pragma unroll
+        for (int u = 0; u < PIECES; ++u) dma_piece(lds + st * STAGE + G::TILE, V, kt * 64, u);
+    };
+
     // All start-up loads are issued before the first wait: this lane's LSE,
     // the first key tile, then this wave's Q, dO and O rows.
     const int qrow = qt * 64 + 32 * lo + n;  // the query this lane owns
     // (the row is clamped rather than the load made conditional: a select
     // right after the load would wait for it)
     const float lse_raw = LSE[f.row_base + min(qrow, S - 1)];
-    u32x4 xk[G::CH], xv[G::CH];
-    f.load(xk, K, 0);
-    f.load(xv, V, 0);
+    dma_tile(0, 0);
     half8 qb[D / 16], ob[D / 16];
     f.grows(qb, Q, qt * 64 + 32 * lo, 0u);
     f.grows(ob, dO, qt * 64 + 32 * lo, 0u);
@@ -86,38 +117,37 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     const int nT = CAUSAL ? qt + 1 : T;
     f.flip(qb, qsign);  // a negative scale negates the logits through Q
     const float lse_q = qrow < S ? lse_raw * kLog2e : 0.f;
-    f.store(lds, xk);
-    f.store(lds + G::TILE, xv);
     int s = 0;
     for (int kt = 0; kt < nT; ++kt) {
-        barrier();
-        const bool more = kt + 1 < nT;
-        if (more) {
-            f.load(xk, K, (kt + 1) * 64);
-            f.load(xv, V, (kt + 1) * 64);
-        }
+        // key tile kt has landed (this wave's loads, then the barrier for
+        // everyone's); every wave is done with tile kt-1, whose stage the
+        // loads of kt+1 overwrite
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + 1 < nT) dma_tile(s ^ 1, kt + 1);
         const _Float16* Ks = lds + s * STAGE;
         const _Float16* Vs = Ks + G::TILE;
         const int k0 = kt * 64 + 32 * hi;  // first key of this wave
 
-        // Every LDS read of the products is issued ahead of its use: with
-        // one wave per SIMD nothing else hides their latency.  The K columns
-        // of dQ += dS K go out while the scores are formed.
-        half8 ak[D / 16], av[D / 16];
-        f.rows(ak, Ks, 32 * hi);
-        f.rows(av, Vs, 32 * hi);
-        __builtin_amdgcn_sched_barrier(0);
+        // Two workgroups per CU: the other one's waves hide the LDS latency,
+        // so the row fragments are read one product at a time (registers).
         floatx16 sacc, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = dp[r] = 0.f;
+        {
+            half8 af[D / 16];
+            f.rows(af, Ks, 32 * hi);
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak[kk], qb[kk], sacc, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk], ob[kk], dp, 0, 0, 0);
+            for (int kk = 0; kk < D / 16; ++kk)
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk], qb[kk], sacc, 0, 0, 0);
+            f.rows(af, Vs, 32 * hi);
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk)
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk], ob[kk], dp, 0, 0, 0);
         }
         half8 bf[2][NB];
         f.cols(bf, Ks, 32 * hi);
-        __builtin_amdgcn_sched_barrier(0);
 
         // register r holds key k0 + 8(r/4) + 4g + r%4 for this lane's query;
         // only the diagonal tile and tiles that reach past S need the mask
@@ -143,10 +173,6 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
 #pragma unroll
             for (int b = 0; b < NB; ++b)
                 dq[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[h][b], sa[h], dq[b], 0, 0, 0);
-        if (more) {
-            f.store(lds + (s ^ 1) * STAGE, xk);
-            f.store(lds + (s ^ 1) * STAGE + G::TILE, xv);
-        }
         s ^= 1;
     }
 
