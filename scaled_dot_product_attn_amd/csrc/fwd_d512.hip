@@ -89,37 +89,49 @@ struct Fwd512 {
     float c;
     uint32_t qsign;
     int tid, w, lane, g, n, rg, dh;
-    u32x4 sreg[G::CH];  // staging registers: K then V of the next tile
+    using LdsPtr = __attribute__((address_space(3))) void*;
 
     __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const _Float16* t, int j0) const {
         return __builtin_amdgcn_make_buffer_rsrc(
             const_cast<_Float16*>(t + base + (size_t)j0 * G::D), (short)0,
             (S - j0) * G::D * 2, 0x00020000);
     }
-    // Next-tile staging: K and V go through the same registers one after the
-    // other (K around the Q K^T phase, V around the P V phase).
-    template <bool IS_V>
-    __device__ __forceinline__ void load_part(int j) {
-        const int j0 = j * G::BN;
-        const auto r = tile_rsrc(IS_V ? V : K, j0);
-#pragma unroll
-        for (int u = 0; u < G::CH; ++u)
-            sreg[u] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (tid + G::NT * u), 0, 0));
-    }
-    template <bool IS_V>
-    __device__ __forceinline__ void store_part(int st) {
+    // Key tile j into LDS stage st, straight from global memory (no staging
+    // registers): one 1 KB load instruction per row (a D = 512 row is 1 KB),
+    // rows 8w .. 8w+7 of K and of V from this wave.  Lane L lands at byte 16 L
+    // of the row: K rows keep their 16-byte pad (M0 = the padded row's
+    // address), V rows are swizzled, so lane L loads the logical chunk the
+    // swizzle puts at physical chunk L.  Rows past S read as zero.  Inline
+    // assembly with M0 = the LDS address, as in the D <= 128 kernel, so the
+    // only waits on these loads are the explicit ones before the barriers.
+    __device__ __forceinline__ void dma_tile(int j, int st) const {
+        // uniform by construction; readfirstlane keeps it (and so the buffer
+        // descriptors) in scalar registers where the loop counter lives in a
+        // vector register
+        const int j0 = __builtin_amdgcn_readfirstlane(j * G::BN);
+        const auto rk = tile_rsrc(K, j0), rv = tile_rsrc(V, j0);
         _Float16* Ks = lds + st * G::STAGE;
         _Float16* Vs = Ks + G::KTILE;
 #pragma unroll
-        for (int u = 0; u < G::CH; ++u) {
-            const int ci = tid + G::NT * u;
-            const int row = ci / G::CPR, cc = ci % G::CPR;
-            if (IS_V)
-                *reinterpret_cast<u32x4*>(Vs + row * G::D + 8 * (cc ^ swz_v512(row))) = sreg[u];
-            else
-                *reinterpret_cast<u32x4*>(Ks + row * G::KSTR + 8 * cc) = sreg[u];
+        for (int u = 0; u < G::BN / G::NW; ++u) {
+            const int row = (G::BN / G::NW) * w + u;
+            const uint32_t mk = (uint32_t)(uintptr_t)(LdsPtr)(Ks + row * G::KSTR);
+            asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :
+                         : "v"((row * G::D + 8 * lane) * 2), "s"(rk), "{m0}"(mk)
+                         : "memory");
+            const uint32_t mv = (uint32_t)(uintptr_t)(LdsPtr)(Vs + row * G::D);
+            asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :
+                         : "v"((row * G::D + 8 * (lane ^ swz_v512(row))) * 2), "s"(rv), "{m0}"(mv)
+                         : "memory");
         }
+    }
+    // This wave's tile loads have landed, then the workgroup barrier.
+    __device__ __forceinline__ void barrier_dma() const {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     }
 
     // Partial S^T over this wave's 256 head dims: 32 keys x 32 queries.
@@ -197,18 +209,16 @@ struct Fwd512 {
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
 
-        load_part<false>(kt0);
-        store_part<false>(0);
-        load_part<true>(kt0);
-        store_part<true>(0);
-        barrier();
+        dma_tile(kt0, 0);
+        barrier_dma();
         float* mine = xch + w * 16 * 64;
         const float* other = xch + (w ^ 2) * 16 * 64;  // same row group, other half
         for (int i = kt0; i < kt1; ++i) {
             const int li = i - kt0;  // LDS stage of tile i: li & 1
             const int j0 = i * G::BN;
-            const int jn = min(i + 1, kt1 - 1);  // past the end: reload the last tile
-            load_part<false>(jn);
+            // the next tile goes into the stage of tile i-1, which every wave
+            // finished before the last barrier
+            if (i + 1 < kt1) dma_tile(i + 1, (li + 1) & 1);
             const bool skip = causal && j0 > r_hi;  // every key is in this wave's future
             floatx16 s;
             if (!skip) {
@@ -218,8 +228,6 @@ struct Fwd512 {
                     *reinterpret_cast<float4*>(mine + (4 * q4) * 64 + 4 * lane) =
                         float4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
             }
-            store_part<false>((li + 1) & 1);  // stage of tile i-1, free since the last barrier
-            load_part<true>(jn);
             barrier();  // both sub-tile partials are published
             if (!skip) {
                 // S = S_0 + S_1 in logit space (the same sum in both waves)
@@ -240,8 +248,7 @@ struct Fwd512 {
                     online_softmax<false, G::DH / 32>(s, lim, c, m, l, o, pf);
                 pv_half(o, pf, li & 1);
             }
-            store_part<true>((li + 1) & 1);
-            barrier();  // next tile in LDS; exchange buffer free again
+            barrier_dma();  // next tile in LDS; exchange buffer free again
         }
 
         // Epilogue: both waves of a row group hold the same m and l; each
