@@ -1,4 +1,4 @@
-"""HIP graph capture of the forward paths: a graph of several calls on
+"""HIP graph capture of every path: a graph of several calls on
 different inputs, replayed several times with eager work and
 synchronisations in between, gives the eager outputs bit for bit on every
 replay.  (bench.py times its K steps as one such graph.)"""
@@ -16,7 +16,7 @@ def _inputs(seed, shape, n):
                   for t in range(3)) for i in range(n)]
 
 
-@pytest.mark.parametrize("path", ["fused", "unfused", "decode"])
+@pytest.mark.parametrize("path", ["fused", "unfused", "decode", "splitkv"])
 def test_graph_replays_match_eager(gpu, path):
     import torch
     if path == "decode":
@@ -26,6 +26,12 @@ def test_graph_replays_match_eager(gpu, path):
         ws = torch.empty(max(gpu.decode_workspace_bytes(B, H, Sq, Sk, D, causal, splits), 1),
                          dtype=torch.uint8, device="cuda")
         qshape = (B, H, Sq, D)
+    elif path == "splitkv":
+        B, H, S, D, causal, sc, splits = 1, 2, 300, 512, True, 0.044, 3
+        sets = _inputs(93_000, (B, H, S, D), 3)
+        ws = torch.empty(gpu.splitkv_workspace_bytes(B, H, S, D, causal, splits),
+                         dtype=torch.uint8, device="cuda")
+        qshape = (B, H, S, D)
     else:
         B, H, S, D, causal, sc = 2, 3, 300, 128, True, 0.088
         sets = _inputs(91_000, (B, H, S, D), 3)
@@ -41,6 +47,9 @@ def test_graph_replays_match_eager(gpu, path):
             gpu.fwd(q, k, v, causal=causal, scale=sc, out=o, lse=lse)
         elif path == "unfused":
             gpu.fwd_unfused(q, k, v, causal=causal, scale=sc, out=o, lse=lse, workspace=ws)
+        elif path == "splitkv":
+            gpu.fwd_splitkv(q, k, v, causal=causal, scale=sc, splits=splits, out=o, lse=lse,
+                            workspace=ws)
         else:
             gpu.fwd_decode(q, k, v, causal=causal, scale=sc, splits=splits, out=o, lse=lse,
                            workspace=ws)
