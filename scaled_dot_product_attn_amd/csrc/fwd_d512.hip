@@ -104,6 +104,7 @@ struct Fwd512 {
     // swizzle puts at physical chunk L.  Rows past S read as zero.  Inline
     // assembly with M0 = the LDS address, as in the D <= 128 kernel, so the
     // only waits on these loads are the explicit ones before the barriers.
+    template <bool DO_K = true, bool DO_V = true>
     __device__ __forceinline__ void dma_tile(int j, int st) const {
         // uniform by construction; readfirstlane keeps it (and so the buffer
         // descriptors) in scalar registers where the loop counter lives in a
@@ -116,12 +117,12 @@ struct Fwd512 {
         for (int u = 0; u < G::BN / G::NW; ++u) {
             const int row = (G::BN / G::NW) * w + u;
             const uint32_t mk = (uint32_t)(uintptr_t)(LdsPtr)(Ks + row * G::KSTR);
-            asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+            if (DO_K) asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                          :
                          : "v"((row * G::D + 8 * lane) * 2), "s"(rk), "{m0}"(mk)
                          : "memory");
             const uint32_t mv = (uint32_t)(uintptr_t)(LdsPtr)(Vs + row * G::D);
-            asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+            if (DO_V) asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                          :
                          : "v"((row * G::D + 8 * (lane ^ swz_v512(row))) * 2), "s"(rv), "{m0}"(mv)
                          : "memory");
@@ -218,7 +219,7 @@ struct Fwd512 {
             const int j0 = i * G::BN;
             // the next tile goes into the stage of tile i-1, which every wave
             // finished before the last barrier
-            if (i + 1 < kt1) dma_tile(i + 1, (li + 1) & 1);
+            if (i + 1 < kt1) dma_tile<true, false>(i + 1, (li + 1) & 1);
             const bool skip = causal && j0 > r_hi;  // every key is in this wave's future
             floatx16 s;
             if (!skip) {
@@ -229,6 +230,7 @@ struct Fwd512 {
                         float4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
             }
             barrier();  // both sub-tile partials are published
+            if (i + 1 < kt1) dma_tile<false, true>(i + 1, (li + 1) & 1);
             if (!skip) {
                 // S = S_0 + S_1 in logit space (the same sum in both waves)
 #pragma unroll
