@@ -14,7 +14,7 @@ import os
 from .build import LIB_PATH
 
 __all__ = ["AttnError", "fwd", "fwd_unfused", "unfused_workspace_bytes", "fwd_splitkv",
-           "splitkv_workspace_bytes", "fwd_decode", "decode_workspace_bytes", "decode_splits", "bwd", "bwd_workspace_bytes", "head_dim_supported", "load_library", "LIB_PATH",
+           "splitkv_workspace_bytes", "splitkv_splits", "fwd_decode", "decode_workspace_bytes", "decode_splits", "bwd", "bwd_workspace_bytes", "head_dim_supported", "load_library", "LIB_PATH",
            "SYMBOLS"]
 
 # Every symbol include/attn.h declares.
@@ -167,15 +167,40 @@ def splitkv_workspace_bytes(B: int, H: int, S: int, D: int, causal: bool, splits
                                                                 splits))
 
 
-def fwd_splitkv(q, k, v, *, causal: bool, splits: int = 4, scale: float | None = None,
+def splitkv_splits(B: int, H: int, S: int, causal: bool, max_units: int = 282) -> int:
+    """A default split count for fwd_splitkv: the largest one (up to 16) whose
+    (batch, head, query tile, chunk) work units still run in about one wave on
+    the 256 CUs of an MI355X (one workgroup per CU, 10% over allowed).  A
+    query tile of 64 rows sees nkt 32-key tiles (all ceil(S/32), or those up
+    to its last row when causal) and is cut into ceil(nkt / C) chunks,
+    C = ceil(ceil(S/32) / splits).  At B1 H8 S1024 causal it picks 3 (264
+    units), measured faster than 2 (192 units) and 4 (320 units)."""
+    nmax = -(-S // 32)
+    tq = -(-S // 64)
+    best = 1
+    for splits in range(1, 17):
+        c = -(-nmax // splits)
+        units = 0
+        for qt in range(tq):
+            kv_end = min(S, 64 * (qt + 1)) if causal else S
+            units += -(-(-(-kv_end // 32)) // c)
+        if B * H * units <= max_units:
+            best = splits
+    return best
+
+
+def fwd_splitkv(q, k, v, *, causal: bool, splits: int | None = None, scale: float | None = None,
                 out=None, lse=None, workspace=None):
     """Split-KV forward (D = 512): every query tile's key range in chunks of
     at most ceil(ceil(S/32) / splits) 32-key tiles, merged in chunk order.
+    ``splits`` defaults to splitkv_splits(B, H, S, causal).
     ``workspace``: a uint8 GPU tensor of at least splitkv_workspace_bytes(...)
     bytes; allocated with torch when not given and needed."""
     import torch
     L = load_library()
     B, H, S, D, out, lse, scale, stream = _prepare(q, k, v, out, lse, scale)
+    if splits is None:
+        splits = splitkv_splits(B, H, S, causal)
     need = splitkv_workspace_bytes(B, H, S, D, causal, splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

@@ -221,3 +221,18 @@ def test_bwd_validation(L):
     assert bwd(ws=o) == C["ATTN_ERR_ALIAS"]          # workspace over an input
     assert bwd(ws=dk) == C["ATTN_ERR_ALIAS"]         # workspace over an output
     assert bwd(lse=dv) == C["ATTN_ERR_ALIAS"]
+
+
+def test_default_split_counts():
+    """Host heuristics for the default split counts: about one wave of
+    workgroups on 256 CUs (decode: doubled while a chunk would exceed 64 key
+    tiles), at least 1, at most one chunk per key tile."""
+    import scaled_dot_product_attn_amd as a
+    assert a.splitkv_splits(1, 8, 1024, True) == 3      # 264 work units
+    assert a.splitkv_splits(4, 16, 2048, True) == 1     # already many query tiles
+    assert a.splitkv_splits(1, 1, 333, True) == 16      # tiny: the cap
+    assert a.decode_splits(1, 32, 1, 4096) == 8
+    assert a.decode_splits(1, 32, 1, 16384) == 8
+    assert a.decode_splits(1, 32, 1, 65536) == 16
+    assert a.decode_splits(8, 32, 4, 8192) == 2
+    assert a.decode_splits(1, 1, 1, 64) == 1            # one key tile
