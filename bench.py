@@ -3,7 +3,13 @@
 
 A step is one attn_fwd call: the whole fused path (load, Q K^T, mask, online
 softmax, P V, normalise, store) over one batch of synthetic inputs already
-resident in HBM.  Prints ONE JSON line.
+resident in HBM.  Prints ONE JSON line.  By default the line is quoted on the
+largest workload, B=8 H=32 S=512 D=128 causal; besides the main (warm)
+record it carries a "cold" record (the same workload cycling through
+--cold-sets copies of its inputs, more bytes between two uses of a set than the
+256 MB Infinity Cache holds), a "workloads" list with every one of the five
+workloads timed the same way, and the shader clock sampled while the timed
+steps ran.
 
     python bench.py [--steps K] [--warmup W] [--workload C] [--rotate R] [--eager]
     python bench.py --suite            # all five workloads, warm and cold
@@ -53,8 +59,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=300)
     p.add_argument("--warmup", type=int, default=30)
-    p.add_argument("--workload", type=int, default=3,
-                   help="1..5 (default 3: B=1 H=32 S=1024 D=128 causal)")
+    p.add_argument("--workload", type=int, default=4,
+                   help="1..5 (default 4: B=8 H=32 S=512 D=128 causal, the largest)")
     p.add_argument("--rotate", type=int, default=1,
                    help="cycle through this many independent input sets")
     p.add_argument("--path", choices=["fused", "unfused", "splitkv", "decode", "bwd"],
@@ -66,8 +72,13 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", action="store_true",
                    help="time the K steps as K host launches instead of one HIP graph replay")
-    p.add_argument("--cpu-seconds", type=float, default=3.0,
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum wall time of the oracle timing loop")
+    p.add_argument("--cold-sets", type=int, default=6,
+                   help="fused path: input buffers cycled by the cold record (each set is "
+                        "a copy of the inputs in its own memory; 0 skips the record)")
+    p.add_argument("--no-workloads", action="store_true",
+                   help="fused path: skip the per-workload records of all five workloads")
     p.add_argument("--suite", action="store_true",
                    help="time all five workloads in one process, interleaved round by round "
                         "(warm and cold), plus the oracle at 1 thread and at all cores; prints "
@@ -277,6 +288,37 @@ def suite(args):
         out["oracle"] = orc
         print(json.dumps(out), flush=True)
 
+def replay_us(step, steps, dev, stream):
+    """Microseconds per step of `steps` calls of step(i) captured once into a
+    HIP graph and replayed: once untimed, then between two events on the
+    launch stream (a synchronize on both sides)."""
+    import torch
+    for i in range(min(steps, 5)):
+        step(i)
+    torch.cuda.synchronize(dev)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize(dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize(dev)
+    del graph
+    return a.elapsed_time(b) * 1e3 / steps
+
+
+def fused_record(w, us):
+    """Per-launch figures of one fused-forward workload at `us` per call."""
+    tf = w.flops() / (us * 1e-6) / 1e12
+    return {"workload": w.name, "us": us, "tflops": tf,
+            "pct_fp16_peak": 100 * tf / PEAK_FP16_TFLOPS,
+            "alg_GBps": w.alg_bytes() / (us * 1e-6) / 1e9}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -364,6 +406,7 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize(dev)
+    sclk = []
 
     # timed region: K back-to-back steps.  By default the K steps are captured
     # once into a HIP graph (every buffer is allocated above; the C ABI
@@ -388,6 +431,7 @@ def main():
         for i in range(args.steps):
             step(i)
     end.record(stream)
+    sclk.append(shader_clock_mhz())  # sampled while the timed steps run
     torch.cuda.synchronize(dev)
     t_wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(end)
@@ -470,6 +514,54 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+    out["sclk_mhz"] = sclk
+    if args.path == "fused" and args.cold_sets > 0:
+        # cold: the calls cycle through cold_sets copies of the inputs, each in
+        # its own memory, so that every call's inputs were last touched
+        # (cold_sets - 1) * input bytes earlier -- past the 256 MB Infinity
+        # Cache when that exceeds it
+        cold = [sets[0]] + [tuple(t.clone() for t in sets[0]) for _ in range(args.cold_sets - 1)]
+
+        def cold_step(i):
+            q, k, v = cold[i % len(cold)]
+            attn.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        nsteps = max(args.steps, 5 * args.cold_sets)
+        us = replay_us(cold_step, nsteps, dev, stream)
+        rec = fused_record(w, us)
+        between = (args.cold_sets - 1) * 3 * w.B * w.H * w.S * w.D * 2
+        rec.update({"input_sets": args.cold_sets, "steps": nsteps,
+                    "input_bytes_between_reuse": between,
+                    "launch": "one HIP graph of the steps, replayed"})
+        # cold, the bytes must come from HBM: the roof is whichever of the
+        # HBM time (algorithmic bytes at 8 TB/s) and the MFMA time is longer
+        hbm_us = w.alg_bytes() / (PEAK_HBM_GBS * 1e9) * 1e6
+        mfma_us = w.flops() / (PEAK_FP16_TFLOPS * 1e12) * 1e6
+        if hbm_us >= mfma_us:
+            gbs = w.alg_bytes() / (us * 1e-6) / 1e9
+            rec["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                               "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}
+        else:
+            rec["roofline"] = {"bound": "mfma", "achieved": rec["tflops"],
+                               "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                               "frac": rec["tflops"] / PEAK_FP16_TFLOPS}
+        del cold
+        out["cold"] = rec
+    if args.path == "fused" and not args.no_workloads:
+        # every workload, warm (same buffers), as a graph replay like the main record
+        recs = []
+        for c, wc in sorted(inputs.WORKLOADS.items()):
+            if c == args.workload:
+                recs.append(fused_record(wc, ms_per_step * 1e3))
+                continue
+            qc, kc, vc = (torch.from_numpy(x).to(dev) for x in wc.qkv())
+            oc = torch.empty(wc.shape, dtype=torch.float16, device=dev)
+            lc = torch.empty(wc.shape[:3], dtype=torch.float32, device=dev)
+
+            def wstep(i, wc=wc, qc=qc, kc=kc, vc=vc, oc=oc, lc=lc):
+                attn.fwd(qc, kc, vc, causal=wc.causal, scale=wc.scale, out=oc, lse=lc)
+            recs.append(fused_record(wc, replay_us(wstep, 100, dev, stream)))
+            del qc, kc, vc, oc, lc
+        out["workloads"] = recs
     if not args.no_cpu_baseline and args.path == "bwd":
         out["cpu_baseline"] = cpu_baseline_bwd(w, args.cpu_seconds)
     elif not args.no_cpu_baseline and not decode:

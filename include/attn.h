@@ -30,8 +30,8 @@
  *   - Accumulation is fp32; P is rounded to fp16 (nearest even) before the
  *     P V product; O is rounded to fp16 (nearest even) once, after dividing
  *     by the row sum.
- *   - Any S >= 1 is accepted: ragged tails are masked, never read out of
- *     bounds.
+ *   - Any S >= 1 is accepted (up to the size limit below): ragged tails are
+ *     masked, never read out of bounds.
  *   - Deterministic: the same inputs give the same output bytes (no atomics,
  *     fixed reduction order).
  *
@@ -58,7 +58,9 @@ extern "C" {
 
 #define ATTN_OK 0
 #define ATTN_ERR_NULL -1      /* a required pointer is NULL */
-#define ATTN_ERR_SHAPE -2     /* B, H or S < 1, or the sizes overflow */
+#define ATTN_ERR_SHAPE -2     /* B, H or S < 1, the sizes overflow 32-bit row
+                                 indices, or one (batch, head) slice of an
+                                 input or output is 4 GiB or more */
 #define ATTN_ERR_HEAD_DIM -3  /* D is not a supported head dimension */
 #define ATTN_ERR_SCALE -4     /* scale is NaN or infinite */
 #define ATTN_ERR_LAUNCH -5    /* the HIP launch failed (see attn_last_hip_error) */

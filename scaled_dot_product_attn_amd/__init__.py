@@ -99,6 +99,23 @@ def unfused_workspace_bytes(B: int, H: int, S: int) -> int:
     return int(load_library().attn_fwd_unfused_workspace_bytes(B, H, S))
 
 
+def _workspace(workspace, need, device):
+    """The workspace tensor to pass (allocated when None and needed), checked
+    to be contiguous device memory on `device`.  Returns (pointer, bytes)."""
+    import torch
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if workspace.device != device:
+        raise ValueError(f"workspace must be on {device}, got {workspace.device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def _prepare(q, k, v, out, lse, scale):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -149,16 +166,12 @@ def fwd_unfused(q, k, v, *, causal: bool, scale: float | None = None, out=None,
     """Unfused three-kernel forward (ablation).  ``workspace``: a uint8 GPU
     tensor of at least unfused_workspace_bytes(B, H, S) bytes; allocated with
     torch when not given."""
-    import torch
     L = load_library()
     B, H, S, D, out, lse, scale, stream = _prepare(q, k, v, out, lse, scale)
-    need = unfused_workspace_bytes(B, H, S)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wptr, wbytes = _workspace(workspace, unfused_workspace_bytes(B, H, S), q.device)
     _check(L.attn_fwd_unfused(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                               lse.data_ptr(), B, H, S, D, int(bool(causal)), scale,
-                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                              stream))
+                              wptr, wbytes, stream))
     return out, lse
 
 
@@ -173,7 +186,7 @@ def splitkv_splits(B: int, H: int, S: int, causal: bool, max_units: int = 282) -
     the 256 CUs of an MI355X (one workgroup per CU, 10% over allowed).  A
     query tile of 64 rows sees nkt 32-key tiles (all ceil(S/32), or those up
     to its last row when causal) and is cut into ceil(nkt / C) chunks,
-    C = ceil(ceil(S/32) / splits).  At B1 H8 S1024 causal it picks 3 (264
+    C = ceil(ceil(S/32) / splits).  At B1 H8 S1024 causal it picks 3 (256
     units), measured faster than 2 (192 units) and 4 (320 units)."""
     nmax = -(-S // 32)
     tq = -(-S // 64)
@@ -196,16 +209,12 @@ def fwd_splitkv(q, k, v, *, causal: bool, splits: int | None = None, scale: floa
     ``splits`` defaults to splitkv_splits(B, H, S, causal).
     ``workspace``: a uint8 GPU tensor of at least splitkv_workspace_bytes(...)
     bytes; allocated with torch when not given and needed."""
-    import torch
     L = load_library()
     B, H, S, D, out, lse, scale, stream = _prepare(q, k, v, out, lse, scale)
     if splits is None:
         splits = splitkv_splits(B, H, S, causal)
-    need = splitkv_workspace_bytes(B, H, S, D, causal, splits)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    wptr = workspace.data_ptr() if workspace is not None else None
-    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    wptr, wbytes = _workspace(workspace, splitkv_workspace_bytes(B, H, S, D, causal, splits),
+                              q.device)
     _check(L.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                               lse.data_ptr(), B, H, S, D, int(bool(causal)), scale, int(splits),
                               wptr, wbytes, stream))
@@ -251,24 +260,25 @@ def fwd_decode(q, k, v, *, causal: bool, splits: int | None = None,
     Sk = k.shape[2]
     if k.shape != v.shape or k.shape[0] != B or k.shape[1] != H or k.shape[3] != D:
         raise ValueError(f"k, v must be [B, H, Sk, D] matching q: {q.shape} {k.shape} {v.shape}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != torch.float16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float16 tensor shaped like q")
+    elif out.shape != q.shape or out.dtype != torch.float16 or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous float16 tensor shaped like q, on q's device")
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    elif lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, Sq]")
+    elif lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, Sq] on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if splits is None:
         splits = decode_splits(B, H, Sq, Sk)
     L = load_library()
-    need = decode_workspace_bytes(B, H, Sq, Sk, D, causal, splits)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    wptr = workspace.data_ptr() if workspace is not None else None
-    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    wptr, wbytes = _workspace(workspace, decode_workspace_bytes(B, H, Sq, Sk, D, causal, splits),
+                              q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(L.attn_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                              lse.data_ptr(), B, H, Sq, Sk, D, int(bool(causal)), float(scale),
@@ -300,12 +310,9 @@ def bwd(q, k, v, o, lse, do, *, causal: bool, scale: float | None = None, dq=Non
             raise ValueError(f"{name} must be a contiguous float16 tensor shaped like q")
         grads.append(t)
     L = load_library()
-    need = bwd_workspace_bytes(B, H, S)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    wbytes = workspace.numel() * workspace.element_size()
+    wptr, wbytes = _workspace(workspace, bwd_workspace_bytes(B, H, S), q.device)
     _check(L.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                       do.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
                       grads[2].data_ptr(), B, H, S, D, int(bool(causal)), scale,
-                      workspace.data_ptr(), wbytes, stream))
+                      wptr, wbytes, stream))
     return tuple(grads)

@@ -78,8 +78,8 @@ struct KvChunking {
     }
     __host__ __device__ int nkt(int qt) const { return (kv_end(qt) + 63) / 64; }
     __host__ __device__ int nchunks(int qt) const { return (nkt(qt) + C - 1) / C; }
-    __host__ __device__ int units() const {
-        int u = 0;
+    __host__ __device__ long long units() const {
+        long long u = 0;
         for (int qt = 0; qt < Tq; ++qt) u += nchunks(qt);
         return u;
     }
@@ -121,7 +121,7 @@ struct Dec {
     __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const _Float16* t, int j0) const {
         return __builtin_amdgcn_make_buffer_rsrc(
             const_cast<_Float16*>(t + kbase + (size_t)j0 * D), (short)0,
-            (Sk - j0) * D * 2, 0x00020000);
+            min(Sk - j0, G::BN) * D * 2, 0x00020000);
     }
     __device__ __forceinline__ void load_tile(int j) {
         const int j0 = j * G::BN;
@@ -412,7 +412,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_dec(const DecArgs& a) {
     using G = GeoD<D>;
     const KvChunking ch = make_kv_chunking(a.Sq, a.Sk, a.causal, a.splits);
-    const int U = ch.units();
+    const int U = (int)ch.units();  // checked to fit by the caller
     const int BH = a.B * a.H;
     const float c = fabsf(a.scale) * 1.44269504088896340736f;
     const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;

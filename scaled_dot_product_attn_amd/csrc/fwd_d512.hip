@@ -22,7 +22,9 @@
 //     kernel.  Splitting P V along the output dims is what the notes call the
 //     pv_n_tile knob; it keeps a wave's output accumulator at 128 registers.
 //   * K (padded rows) and V (XOR-swizzled rows) stream through two LDS stages,
-//     staged through registers with bounds-checked buffer loads.
+//     loaded straight from global memory into LDS (bounds-checked buffer loads
+//     with the LDS destination bit, one 1 KB row per instruction, no staging
+//     registers).
 //
 // Split-KV.  Eight heads of 1024 rows give only 128 workgroups for 256 CUs, and
 // under causal masking the last query tile does 32 key tiles while the first
@@ -94,7 +96,7 @@ struct Fwd512 {
     __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const _Float16* t, int j0) const {
         return __builtin_amdgcn_make_buffer_rsrc(
             const_cast<_Float16*>(t + base + (size_t)j0 * G::D), (short)0,
-            (S - j0) * G::D * 2, 0x00020000);
+            min(S - j0, G::BN) * G::D * 2, 0x00020000);
     }
     // Key tile j into LDS stage st, straight from global memory (no staging
     // registers): one 1 KB load instruction per row (a D = 512 row is 1 KB),
@@ -303,8 +305,8 @@ struct Chunking {
         return (kv_end + G512::BN - 1) / G512::BN;
     }
     __host__ __device__ int nchunks(int qt) const { return (nkt(qt) + C - 1) / C; }
-    __host__ __device__ int units() const {
-        int u = 0;
+    __host__ __device__ long long units() const {
+        long long u = 0;
         for (int qt = 0; qt < T; ++qt) u += nchunks(qt);
         return u;
     }
@@ -439,7 +441,7 @@ Chunking make_chunking(int S, int causal, int splits) {
 hipError_t launch(const FwdArgs& a, int splits, float* ws) {
     using G = G512;
     const Chunking ch = make_chunking(a.S, a.causal, splits);
-    const int U = ch.units();
+    const int U = (int)ch.units();  // checked to fit by the caller
     const int BH = a.B * a.H;
     const float c = fabsf(a.scale) * 1.44269504088896340736f;
     const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;

@@ -168,7 +168,7 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
     u32x4 st[G::CH];
     auto load = [&](int t) {
         const int j0 = t * G::BN;
-        const auto r = rsrc(V + vbase + (size_t)j0 * D, (uint32_t)(S - j0) * D * 2);
+        const auto r = rsrc(V + vbase + (size_t)j0 * D, (uint32_t)min(S - j0, G::BN) * D * 2);
 #pragma unroll
         for (int u = 0; u < G::CH; ++u)
             st[u] = __builtin_bit_cast(

@@ -228,7 +228,7 @@ def test_default_split_counts():
     workgroups on 256 CUs (decode: doubled while a chunk would exceed 64 key
     tiles), at least 1, at most one chunk per key tile."""
     import scaled_dot_product_attn_amd as a
-    assert a.splitkv_splits(1, 8, 1024, True) == 3      # 264 work units
+    assert a.splitkv_splits(1, 8, 1024, True) == 3      # 256 work units
     assert a.splitkv_splits(4, 16, 2048, True) == 1     # already many query tiles
     assert a.splitkv_splits(1, 1, 333, True) == 16      # tiny: the cap
     assert a.decode_splits(1, 32, 1, 4096) == 8
@@ -236,3 +236,47 @@ def test_default_split_counts():
     assert a.decode_splits(1, 32, 1, 65536) == 16
     assert a.decode_splits(8, 32, 4, 8192) == 2
     assert a.decode_splits(1, 1, 1, 64) == 1            # one key tile
+
+
+def test_slice_of_4gib_is_rejected(L):
+    """Buffer descriptors address one (batch, head) slice with 32-bit byte
+    offsets, so every entry point rejects a slice of 4 GiB or more before any
+    launch (the largest accepted slice is one row less)."""
+    big = 0x1_0000_0000_0000  # fake, far apart: validation never dereferences them
+    q, k, v, o, lse = (big * (i + 1) for i in range(5))
+    fw = lambda S, D: L.attn_fwd(q, k, v, o, lse, 1, 1, S, D, 1, 0.1, None)
+    assert fw(1 << 24, 128) == C["ATTN_ERR_SHAPE"]          # 16M rows x 256 B = 4 GiB
+    assert fw(1 << 22, 512) == C["ATTN_ERR_SHAPE"]          # 4M rows x 1 KB
+    assert fw(1 << 25, 64) == C["ATTN_ERR_SHAPE"]
+    W = big * 7
+    assert L.attn_fwd_unfused(q, k, v, o, lse, 1, 1, 1 << 22, 512, 1, 0.1, W, 1 << 62,
+                              None) == C["ATTN_ERR_SHAPE"]
+    dec = lambda Sq, Sk: L.attn_fwd_decode(q, k, v, o, lse, 1, 1, Sq, Sk, 128, 1, 0.1, 1,
+                                           W, 1 << 62, None)
+    assert dec(1, 1 << 24) == C["ATTN_ERR_SHAPE"]           # the K/V cache slice
+    bwd = L.attn_bwd(q, k, v, o, lse, big * 6, big * 8, big * 9, big * 10, 1, 1, 1 << 24, 128,
+                     1, 0.1, W, 1 << 62, None)
+    assert bwd == C["ATTN_ERR_SHAPE"]
+
+
+def test_unit_counts_do_not_wrap(L):
+    """The (query tile, key chunk) unit count of a long causal row with many
+    splits exceeds 2^31; the library counts it in 64 bits, so the workspace
+    size is exact and the launch is refused instead of running a wrapped
+    grid."""
+    S, splits = (1 << 22) - 64, 1 << 20      # D = 512: just under a 4 GiB slice
+    units, T = splitkv_units(S, 1, splits)
+    assert units > 2**31
+    slot = (64 * 512 + 2 * 64) * 4
+    assert L.attn_fwd_splitkv_workspace_bytes(1, 1, S, 512, 1, splits) == units * slot
+    big = 0x1_0000_0000_0000
+    q, k, v, o, lse = (big * (i + 1) for i in range(5))
+    assert L.attn_fwd_splitkv(q, k, v, o, lse, 1, 1, S, 512, 1, 0.1, splits, big * 7,
+                              units * slot, None) == C["ATTN_ERR_SHAPE"]
+    Sq = Sk = (1 << 24) - 64                 # D = 128, decode form, 64-key tiles
+    du, Tq = decode_units(Sq, Sk, 1, 1 << 20)
+    assert du > 2**31
+    assert L.attn_fwd_decode_workspace_bytes(1, 1, Sq, Sk, 128, 1, 1 << 20) == \
+        du * (64 * 128 + 128) * 4
+    assert L.attn_fwd_decode(q, k, v, o, lse, 1, 1, Sq, Sk, 128, 1, 0.1, 1 << 20, big * 7,
+                             1 << 62, None) == C["ATTN_ERR_SHAPE"]

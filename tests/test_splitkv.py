@@ -24,9 +24,12 @@ def run_split(gpu, q, k, v, causal, scale, splits):
     return o.cpu().numpy(), lse.cpu().numpy()
 
 
-@pytest.mark.parametrize("splits", [2, 4, 7])
+# None: the binding's default count (splitkv_splits), the one bench.py times
+@pytest.mark.parametrize("splits", [2, 3, 4, 7, None])
 def test_splitkv_workload5(gpu, oracle_mod, splits):
     w = inputs.WORKLOADS[5]
+    if splits is None:
+        assert gpu.splitkv_splits(w.B, w.H, w.S, w.causal) == 3
     log(f"split-KV {w.name} splits={splits}")
     q, k, v = w.qkv()
     o, lse = run_split(gpu, q, k, v, w.causal, w.scale, splits)
