@@ -18,6 +18,9 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
+// Buffer descriptors address one (batch, head) slice with 32-bit offsets.
+constexpr long long kMaxSliceBytes = 1LL << 32;
+
 // Shared argument checks of the fused and unfused forward.
 int validate(const void* q, const void* k, const void* v, const void* o,
              const float* lse, int B, int H, int S, int D, float scale) {
@@ -26,7 +29,7 @@ int validate(const void* q, const void* k, const void* v, const void* o,
     // Kernels index rows with 32-bit ints and launch B*H*ceil(S/32) groups at most.
     const long long bh = (long long)B * H;
     if (bh > INT32_MAX || (long long)S > INT32_MAX / 2 || bh * S > INT32_MAX ||
-        bh * ((S + 31) / 32) > INT32_MAX)
+        bh * ((S + 31) / 32) > INT32_MAX || (long long)S * D * 2 >= kMaxSliceBytes)
         return ATTN_ERR_SHAPE;
     if (!attn_head_dim_supported(D)) return ATTN_ERR_HEAD_DIM;
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
@@ -55,6 +58,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     if (st != ATTN_OK) return st;
     const attn::FwdArgs a{q, k, v, o, lse, B, H, S, D, causal != 0, scale, stream};
     if (D == 512) return launched(attn::launch_fused_d512(a));
+    // D = 128 with enough 128-row query tiles for two workgroups on every CU
+    // of the 256: the 128-row kernel (half the staged bytes per FLOP, no key
+    // merge); otherwise the 64-row kernel, whose waves split the keys of a
+    // tile and so keep every CU busy on fewer rows
+    if (D == 128 && (long long)B * H * ((S + 127) / 128) >= 512)
+        return launched(attn::launch_fused_rows_d128(a));
     return launched(attn::launch_fused_pipe_d64_d128(a));
 }
 
@@ -125,7 +134,8 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
     if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1) return ATTN_ERR_SHAPE;
     const long long bh = (long long)B * H;
     if (bh > INT32_MAX || bh * Sq > INT32_MAX / 2 || bh * Sk > INT32_MAX / 2 ||
-        (causal && Sq > Sk))
+        (causal && Sq > Sk) || (long long)Sq * D * 2 >= kMaxSliceBytes ||
+        (long long)Sk * D * 2 >= kMaxSliceBytes)
         return ATTN_ERR_SHAPE;
     if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
@@ -165,7 +175,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     const long long bh = (long long)B * H;
     // rows are indexed with 32-bit ints; one workgroup per (batch, head, 64-row tile)
     if (bh > INT32_MAX || (long long)S > INT32_MAX / 2 || bh * S > INT32_MAX / 2 ||
-        bh * ((S + 63) / 64) > INT32_MAX)
+        bh * ((S + 63) / 64) > INT32_MAX || (long long)S * D * 2 >= kMaxSliceBytes)
         return ATTN_ERR_SHAPE;
     if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
@@ -192,11 +202,14 @@ const char* attn_status_string(int status) {
     switch (status) {
         case ATTN_OK: return "ok";
         case ATTN_ERR_NULL: return "a required pointer is NULL";
-        case ATTN_ERR_SHAPE: return "B, H and S must be >= 1 and the sizes must fit 32-bit row indices";
+        case ATTN_ERR_SHAPE:
+            return "B, H and S must be >= 1, the sizes must fit 32-bit row indices and one "
+                   "(batch, head) slice must stay under 4 GiB";
         case ATTN_ERR_HEAD_DIM: return "unsupported head dimension (supported: 64, 128, 512)";
         case ATTN_ERR_SCALE: return "scale must be finite";
         case ATTN_ERR_LAUNCH: return "HIP kernel launch failed (see attn_last_hip_error)";
-        case ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_fwd_unfused_workspace_bytes";
+        case ATTN_ERR_WORKSPACE:
+            return "workspace is NULL or smaller than the entry point's *_workspace_bytes size";
         case ATTN_ERR_ALIAS: return "an output buffer overlaps another buffer";
         case ATTN_ERR_SPLITS: return "splits must be >= 1";
         default: return "unknown status";

@@ -97,5 +97,89 @@ __device__ __forceinline__ void online_softmax(floatx16 s, int lim, float c, flo
     l += psum;
 }
 
+// Online softmax of one 32-key x 32-query S^T block (register r of lane
+// (g, n): key 8(r/4) + 4g + r%4 of the block, query n; keys with
+// 8(r/4) + r%4 > lim are masked when MASK).  c = |scale| log2(e); m: the
+// running reference max (log2 units), l: this lane's share of the row sum,
+// o: the output blocks.  P^T (fp16, round to nearest even) goes to pf as the
+// B operand of the two 16-key P V steps.
+//
+// The weights are formed against the current reference max m without
+// looking at the row max.  Every weight is at most the lane's sum of them, so
+// while every lane's sum stays within 2^kLazyTau no weight exceeds it and
+// nothing else is done; otherwise (or when the sum is NaN: m = -inf meeting a
+// masked key) the row max is taken, the reference moves to it, the output and
+// sum are rescaled and the weights formed again.  So the row-max tree runs
+// only on the rare blocks that move the reference, and every weight stays
+// <= 2^kLazyTau (fp16-safe) either way.  The sum runs as a tree (short
+// dependence chains), and the speculative weights are pinned ahead of the
+// branch so that they stay in the same scheduling region as the next tile's
+// matrix instructions.
+constexpr float kLazyBound = 256.0f;  // 2^kLazyTau
+static_assert(kLazyTau == 8.0f, "kLazyBound = 2^kLazyTau");
+template <bool MASK, int NB, bool PIPE>
+__device__ __forceinline__ void softmax_block(floatx16 s, int lim, float c, float& m, float& l,
+                                              floatx16* o, half8* pf) {
+    if (MASK) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if ((8 * (r >> 2) + (r & 3)) > lim) s[r] = kNegInf;
+    }
+    // weights against reference mref: P^T in fp16 into pf, and this lane's
+    // sum in fp32 (four partial sums, then a tree)
+    auto weights = [&](float mref) {
+        float q[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float t = __builtin_fmaf(s[r], c, -mref);
+            if (MASK && (8 * (r >> 2) + (r & 3)) > lim) t = kNegInf;
+            const float e = __builtin_amdgcn_exp2f(t);
+            q[r & 3] += e;
+            pf[r >> 3][r & 7] = (_Float16)e;
+        }
+        return (q[0] + q[1]) + (q[2] + q[3]);
+    };
+    float psum = weights(m);
+    // keep the speculative weights ahead of the branch
+    asm volatile("" : "+v"(psum));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        u32x4 x = __builtin_bit_cast(u32x4, pf[h]);
+        asm volatile("" : "+v"(x));
+        pf[h] = __builtin_bit_cast(half8, x);
+    }
+    if (PIPE) {
+        // interleave the next tile's Q K^T (8 MFMAs, issued by the caller in
+        // this region) with this softmax's vector work
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+        }
+    }
+    // every weight is at most the lane's sum; the sum is NaN when m = -inf
+    // meets a masked key (-inf + inf), and that too takes the branch
+    if (__builtin_amdgcn_ballot_w64(!(psum <= kLazyBound)) != 0) {
+        const float mx = fmaxf(fmaxf(fmaxf(fmaxf(s[0], s[1]), s[2]), fmaxf(fmaxf(s[3], s[4]), s[5])),
+                               fmaxf(fmaxf(fmaxf(s[6], s[7]), s[8]),
+                                     fmaxf(fmaxf(fmaxf(s[9], s[10]), s[11]),
+                                           fmaxf(fmaxf(fmaxf(s[12], s[13]), s[14]), s[15]))));
+        // fmaxf keeps the candidate finite when every key is masked
+        // (c * -inf) or c == 0 (0 * -inf)
+        const float cand = fmaxf(c * max_halves(mx), -kFltMax);
+        const float m_new = fmaxf(m, cand);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        m = m_new;
+        l *= alpha;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
+        psum = weights(m);
+    }
+    l += psum;
+}
+
 }  // namespace detail
 }  // namespace attn

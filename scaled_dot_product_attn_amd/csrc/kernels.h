@@ -20,6 +20,10 @@ struct FwdArgs {
 // query tile, two per CU, K/V tiles loaded straight into LDS, the next tile's
 // Q K^T overlapped with the current tile's softmax.
 hipError_t launch_fused_pipe_d64_d128(const FwdArgs& a);
+// Fused single-kernel forward, D = 128, for shapes with many query tiles: one
+// workgroup of four waves per 128-row query tile, two per CU, every wave
+// owning 32 complete rows and walking the keys in 32-key chunks.
+hipError_t launch_fused_rows_d128(const FwdArgs& a);
 // Fused single-kernel forward, D = 512 (head-dim halves summed in logit space).
 hipError_t launch_fused_d512(const FwdArgs& a);
 // Split-KV forward, D = 512: every query tile's key range cut into chunks of
