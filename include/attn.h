@@ -67,6 +67,12 @@ extern "C" {
 #define ATTN_ERR_WORKSPACE -6 /* workspace NULL or smaller than required */
 #define ATTN_ERR_ALIAS -7     /* an output buffer overlaps another buffer */
 #define ATTN_ERR_SPLITS -8    /* splits < 1 */
+#define ATTN_ERR_SCRATCH -9   /* attn_fwd_decode_noalloc: the call needs more than
+                                 ATTN_DECODE_NOALLOC_SCRATCH_BYTES of workspace */
+
+/* Capacity of the static device scratch array behind attn_fwd_decode_noalloc
+   (32 MiB per GPU). */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 /*
  * Fused forward: one kernel, scores kept on chip.
@@ -157,6 +163,27 @@ size_t attn_fwd_decode_workspace_bytes(int B, int H, int Sq, int Sk, int D, int 
 int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int H, int Sq, int Sk, int D, int causal, float scale, int splits,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results (bit for bit) and launches as attn_fwd_decode,
+ * without the workspace: the chunks' partial states go to a static device
+ * array of ATTN_DECODE_NOALLOC_SCRATCH_BYTES that each GPU holds from the
+ * library's first use of it until the process ends.  Nothing is allocated
+ * and nothing freed.
+ *   - A call needing more than ATTN_DECODE_NOALLOC_SCRATCH_BYTES (see
+ *     attn_fwd_decode_workspace_bytes) returns ATTN_ERR_SCRATCH before any
+ *     launch.
+ *   - All calls on one GPU share its array.  Calls whose execution overlaps
+ *     on one GPU (e.g. on two unordered streams) race on it and give wrong
+ *     results; calls ordered on one stream are safe.
+ *   - The first call on a device looks up the array's device address (a
+ *     HIP symbol query, no allocation); its failure is ATTN_ERR_LAUNCH.
+ */
+int attn_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int Sq, int Sk, int D, int causal, float scale,
+                            int splits, void* stream);
 
 /*
  * Backward of attn_fwd for D = 64 or 128: the gradients of L = sum(dO * O)

@@ -14,17 +14,21 @@ import os
 from .build import LIB_PATH
 
 __all__ = ["AttnError", "fwd", "fwd_unfused", "unfused_workspace_bytes", "fwd_splitkv",
-           "splitkv_workspace_bytes", "splitkv_splits", "fwd_decode", "decode_workspace_bytes", "decode_splits", "bwd", "bwd_workspace_bytes", "head_dim_supported", "load_library", "LIB_PATH",
+           "splitkv_workspace_bytes", "splitkv_splits", "fwd_decode", "fwd_decode_noalloc", "decode_workspace_bytes", "decode_splits",
+           "DECODE_NOALLOC_SCRATCH_BYTES", "bwd", "bwd_workspace_bytes", "head_dim_supported", "load_library", "LIB_PATH",
            "SYMBOLS"]
 
 # Every symbol include/attn.h declares.
 SYMBOLS = ("attn_fwd", "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
            "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
-           "attn_fwd_decode", "attn_fwd_decode_workspace_bytes",
+           "attn_fwd_decode", "attn_fwd_decode_workspace_bytes", "attn_fwd_decode_noalloc",
            "attn_bwd", "attn_bwd_workspace_bytes",
            "attn_head_dim_supported", "attn_status_string", "attn_last_hip_error")
 
 ATTN_ERR_LAUNCH = -5
+ATTN_ERR_SCRATCH = -9
+# capacity of the static scratch array behind fwd_decode_noalloc (attn.h)
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class AttnError(RuntimeError):
@@ -66,6 +70,8 @@ def load_library(path: str = LIB_PATH):
     L.attn_fwd_splitkv_workspace_bytes.restype = Z
     L.attn_fwd_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
     L.attn_fwd_decode.restype = I
+    L.attn_fwd_decode_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P]
+    L.attn_fwd_decode_noalloc.restype = I
     L.attn_fwd_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     L.attn_fwd_decode_workspace_bytes.restype = Z
     L.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, Z, P]
@@ -243,11 +249,7 @@ def decode_splits(B: int, H: int, Sq: int, Sk: int, target_units: int = 256,
     return max(1, min(k_tiles, splits))
 
 
-def fwd_decode(q, k, v, *, causal: bool, splits: int | None = None,
-               scale: float | None = None, out=None, lse=None, workspace=None):
-    """Decode form: q [B, H, Sq, D] against k, v [B, H, Sk, D] (contiguous fp16
-    on the GPU, D = 64 or 128); causal aligned bottom-right.  Returns
-    (o fp16 [B, H, Sq, D], lse fp32 [B, H, Sq])."""
+def _decode_args(q, k, v, out, lse, scale, splits, causal):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor):
@@ -276,13 +278,38 @@ def fwd_decode(q, k, v, *, causal: bool, splits: int | None = None,
         scale = 1.0 / math.sqrt(D)
     if splits is None:
         splits = decode_splits(B, H, Sq, Sk)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    return B, H, Sq, Sk, D, out, lse, float(scale), int(splits), stream
+
+
+def fwd_decode(q, k, v, *, causal: bool, splits: int | None = None,
+               scale: float | None = None, out=None, lse=None, workspace=None):
+    """Decode form: q [B, H, Sq, D] against k, v [B, H, Sk, D] (contiguous fp16
+    on the GPU, D = 64 or 128); causal aligned bottom-right.  Returns
+    (o fp16 [B, H, Sq, D], lse fp32 [B, H, Sq])."""
+    B, H, Sq, Sk, D, out, lse, scale, splits, stream = _decode_args(q, k, v, out, lse, scale,
+                                                                    splits, causal)
     L = load_library()
     wptr, wbytes = _workspace(workspace, decode_workspace_bytes(B, H, Sq, Sk, D, causal, splits),
                               q.device)
-    stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(L.attn_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                             lse.data_ptr(), B, H, Sq, Sk, D, int(bool(causal)), float(scale),
-                             int(splits), wptr, wbytes, stream))
+                             lse.data_ptr(), B, H, Sq, Sk, D, int(bool(causal)), scale,
+                             splits, wptr, wbytes, stream))
+    return out, lse
+
+
+def fwd_decode_noalloc(q, k, v, *, causal: bool, splits: int | None = None,
+                       scale: float | None = None, out=None, lse=None):
+    """fwd_decode without a workspace: the library's static per-GPU scratch
+    array (DECODE_NOALLOC_SCRATCH_BYTES) holds the chunks' partial states, and
+    the C entry point allocates nothing (pass out and lse to keep torch from
+    allocating them).  Calls that overlap on one GPU race on the array."""
+    B, H, Sq, Sk, D, out, lse, scale, splits, stream = _decode_args(q, k, v, out, lse, scale,
+                                                                    splits, causal)
+    L = load_library()
+    _check(L.attn_fwd_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), B, H, Sq, Sk, D, int(bool(causal)), scale,
+                                     splits, stream))
     return out, lse
 
 

@@ -41,6 +41,33 @@ int validate(const void* q, const void* k, const void* v, const void* o,
     return ATTN_OK;
 }
 
+// Argument checks shared by the two decode entry points (everything but the
+// workspace).
+int validate_decode(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, int B, int H, int Sq, int Sk, int D, int causal,
+                    float scale, int splits) {
+    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+    if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1) return ATTN_ERR_SHAPE;
+    const long long bh = (long long)B * H;
+    if (bh > INT32_MAX || bh * Sq > INT32_MAX / 2 || bh * Sk > INT32_MAX / 2 ||
+        (causal && Sq > Sk) || (long long)Sq * D * 2 >= kMaxSliceBytes ||
+        (long long)Sk * D * 2 >= kMaxSliceBytes)
+        return ATTN_ERR_SHAPE;
+    if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+    if (!isfinite(scale)) return ATTN_ERR_SCALE;
+    if (splits < 1) return ATTN_ERR_SPLITS;
+    if (bh * attn::decode_units(Sq, Sk, causal != 0, splits) > INT32_MAX ||
+        bh * ((Sq + 63) / 64) * 8 > INT32_MAX)
+        return ATTN_ERR_SHAPE;
+    const size_t nq = (size_t)bh * Sq * D * 2, nk = (size_t)bh * Sk * D * 2,
+                 nl = (size_t)bh * Sq * 4;
+    if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nk) || overlaps(o, nq, v, nk) ||
+        overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nk) ||
+        overlaps(lse, nl, o, nq))
+        return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
 int launched(hipError_t e) {
     g_last_hip_error = (int)e;
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
@@ -130,25 +157,11 @@ size_t attn_fwd_decode_workspace_bytes(int B, int H, int Sq, int Sk, int D, int 
 int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int H, int Sq, int Sk, int D, int causal, float scale, int splits,
                     void* workspace, size_t workspace_bytes, void* stream) {
-    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
-    if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1) return ATTN_ERR_SHAPE;
+    const int st = validate_decode(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, splits);
+    if (st != ATTN_OK) return st;
     const long long bh = (long long)B * H;
-    if (bh > INT32_MAX || bh * Sq > INT32_MAX / 2 || bh * Sk > INT32_MAX / 2 ||
-        (causal && Sq > Sk) || (long long)Sq * D * 2 >= kMaxSliceBytes ||
-        (long long)Sk * D * 2 >= kMaxSliceBytes)
-        return ATTN_ERR_SHAPE;
-    if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
-    if (!isfinite(scale)) return ATTN_ERR_SCALE;
-    if (splits < 1) return ATTN_ERR_SPLITS;
-    if (bh * attn::decode_units(Sq, Sk, causal != 0, splits) > INT32_MAX ||
-        bh * ((Sq + 63) / 64) * 8 > INT32_MAX)
-        return ATTN_ERR_SHAPE;
     const size_t nq = (size_t)bh * Sq * D * 2, nk = (size_t)bh * Sk * D * 2,
                  nl = (size_t)bh * Sq * 4;
-    if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nk) || overlaps(o, nq, v, nk) ||
-        overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nk) ||
-        overlaps(lse, nl, o, nq))
-        return ATTN_ERR_ALIAS;
     const size_t need = attn_fwd_decode_workspace_bytes(B, H, Sq, Sk, D, causal, splits);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
@@ -159,6 +172,23 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
     }
     const attn::DecArgs a{q, k, v, o, lse, B, H, Sq, Sk, D, causal != 0, scale, splits,
                           need > 0 ? workspace : nullptr, stream};
+    return launched(attn::launch_decode(a));
+}
+
+int attn_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int Sq, int Sk, int D, int causal, float scale,
+                            int splits, void* stream) {
+    const int st = validate_decode(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, splits);
+    if (st != ATTN_OK) return st;
+    const size_t need = attn_fwd_decode_workspace_bytes(B, H, Sq, Sk, D, causal, splits);
+    if (need > ATTN_DECODE_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+    void* scratch = nullptr;
+    if (need > 0) {
+        const hipError_t e = attn::decode_scratch(&scratch);
+        if (e != hipSuccess) return launched(e);
+    }
+    const attn::DecArgs a{q, k, v, o, lse, B, H, Sq, Sk, D, causal != 0, scale, splits,
+                          scratch, stream};
     return launched(attn::launch_decode(a));
 }
 
@@ -212,6 +242,9 @@ const char* attn_status_string(int status) {
             return "workspace is NULL or smaller than the entry point's *_workspace_bytes size";
         case ATTN_ERR_ALIAS: return "an output buffer overlaps another buffer";
         case ATTN_ERR_SPLITS: return "splits must be >= 1";
+        case ATTN_ERR_SCRATCH:
+            return "the call needs more workspace than the static scratch array holds "
+                   "(ATTN_DECODE_NOALLOC_SCRATCH_BYTES): use attn_fwd_decode with a workspace";
         default: return "unknown status";
     }
 }

@@ -32,6 +32,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
+#include "attn.h"
+
 #include "fwd_common.h"
 #include "kernels.h"
 
@@ -438,6 +442,36 @@ size_t decode_workspace_floats(int B, int H, int Sq, int Sk, int D, int causal, 
     const KvChunking ch = make_kv_chunking(Sq, Sk, causal, splits);
     if (ch.units() == ch.Tq) return 0;  // no query tile is split
     return (size_t)B * H * ch.units() * ((size_t)64 * D + 128);
+}
+
+// The workspace of attn_fwd_decode_noalloc: a static device array, so that a
+// caller that cannot allocate (code under HIP graph capture, a tight serving
+// loop) still gets the split-key path.  Each GPU the library runs on holds its
+// own copy until the process ends.  Every call on a GPU shares it and every
+// call writes each slot it later reads, so nothing needs clearing; calls that
+// overlap on one GPU (different streams, no ordering) race on it.
+static __device__ __align__(256) float scratch[ATTN_DECODE_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+hipError_t decode_scratch(void** ptr) {
+    // In host code `scratch` names a host-side stand-in, not device memory:
+    // the address kernels may use comes from hipGetSymbolAddress, once per
+    // device with that device current, kept per device.
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_decode(const DecArgs& a) {

@@ -51,6 +51,10 @@ struct DecArgs {
     void* stream;
 };
 hipError_t launch_decode(const DecArgs& a);
+// The decode workspace that needs no allocation: a static device array of
+// ATTN_DECODE_NOALLOC_SCRATCH_BYTES, one per GPU.  *ptr = its address on the
+// current device (looked up once per device, then cached).
+hipError_t decode_scratch(void** ptr);
 // Work units per (batch, head) and workspace floats (0 when no query tile is
 // split) of launch_decode.
 long long decode_units(int Sq, int Sk, int causal, int splits);

@@ -280,3 +280,27 @@ def test_unit_counts_do_not_wrap(L):
         du * (64 * 128 + 128) * 4
     assert L.attn_fwd_decode(q, k, v, o, lse, 1, 1, Sq, Sk, 128, 1, 0.1, 1 << 20, big * 7,
                              1 << 62, None) == C["ATTN_ERR_SHAPE"]
+
+
+def test_decode_noalloc_validation(L):
+    """attn_fwd_decode_noalloc: the decode checks, and ATTN_ERR_SCRATCH for a
+    call whose workspace would exceed the static array, all before any HIP
+    call."""
+    cap = 32 << 20
+    big = 0x1_0000_0000_0000  # fake, far apart: validation never dereferences them
+    q_, k_, v_, o_, l_ = (big * (i + 1) for i in range(5))
+    def nd(q=q_, k=k_, v=v_, o=o_, lse=l_, B=1, H=64, Sq=1, Sk=65536, D=128, causal=1,
+           scale=0.1, splits=64):
+        return L.attn_fwd_decode_noalloc(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale,
+                                         splits, None)
+    assert L.attn_fwd_decode_workspace_bytes(1, 64, 1, 65536, 128, 1, 64) > cap
+    assert nd() == C["ATTN_ERR_SCRATCH"]
+    assert nd(q=None) == C["ATTN_ERR_NULL"]
+    assert nd(D=512) == C["ATTN_ERR_HEAD_DIM"]
+    assert nd(Sq=5, Sk=4) == C["ATTN_ERR_SHAPE"]
+    assert nd(splits=0) == C["ATTN_ERR_SPLITS"]
+    assert nd(scale=math.nan) == C["ATTN_ERR_SCALE"]
+    assert nd(lse=o_) == C["ATTN_ERR_ALIAS"]
+    s = L.attn_status_string(C["ATTN_ERR_SCRATCH"]).decode()
+    assert "scratch" in s
+    assert attn.DECODE_NOALLOC_SCRATCH_BYTES == cap
