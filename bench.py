@@ -311,12 +311,27 @@ def replay_us(step, steps, dev, stream):
     return a.elapsed_time(b) * 1e3 / steps
 
 
+def binding_roof(flops, nbytes, us):
+    """The roofline of a launch of `flops` and `nbytes` algorithmic bytes that
+    takes `us`: the roof whose time at peak is the longer one (FLOPs at the
+    FP16 MFMA peak, or the bytes at the HBM peak), and the fraction of it
+    reached."""
+    if flops / (PEAK_FP16_TFLOPS * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9):
+        a = flops / (us * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": a, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                "frac": a / PEAK_FP16_TFLOPS}
+    a = nbytes / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": a / PEAK_HBM_GBS}
+
+
 def fused_record(w, us):
     """Per-launch figures of one fused-forward workload at `us` per call."""
     tf = w.flops() / (us * 1e-6) / 1e12
     return {"workload": w.name, "us": us, "tflops": tf,
             "pct_fp16_peak": 100 * tf / PEAK_FP16_TFLOPS,
-            "alg_GBps": w.alg_bytes() / (us * 1e-6) / 1e9}
+            "alg_GBps": w.alg_bytes() / (us * 1e-6) / 1e9,
+            "roofline": binding_roof(w.flops(), w.alg_bytes(), us)}
 
 
 def main():
@@ -465,16 +480,11 @@ def main():
     # back to back between two events on the launch stream); bracketing each
     # call with its own events adds the launch latency to every call
     step_us = ms_per_step * 1e3
-    achieved = flops / (step_us * 1e-6) / 1e12
-    # the square D=128/512 causal shapes sit near the ridge; decode streams K/V
-    bound_mfma = not decode and w.D >= 128 and w.causal
-    if bound_mfma:
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_FP16_TFLOPS, "traffic": None}
-    else:
-        gbs = nbytes / (step_us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": gbs / PEAK_HBM_GBS, "traffic": None}
+    # the binding roof: causal attention does 2 S^2 D FLOPs on 8 S D bytes per
+    # (batch, head), S/4 FLOP per byte, under the FP16/HBM ridge (~315) for
+    # S < 1260, so every causal workload here is HBM-bound on the roofline;
+    # pct_fp16_peak below keeps the MFMA fraction
+    roof = binding_roof(flops, nbytes, step_us)
     roof["traffic"] = measured_traffic(w.name, args.path)
     roof["launch_us"] = step_us
     roof["launches_per_step"] = {"fused": 1, "unfused": 3, "splitkv": 2, "decode": 1 if not decode or
@@ -532,18 +542,6 @@ def main():
         rec.update({"input_sets": args.cold_sets, "steps": nsteps,
                     "input_bytes_between_reuse": between,
                     "launch": "one HIP graph of the steps, replayed"})
-        # cold, the bytes must come from HBM: the roof is whichever of the
-        # HBM time (algorithmic bytes at 8 TB/s) and the MFMA time is longer
-        hbm_us = w.alg_bytes() / (PEAK_HBM_GBS * 1e9) * 1e6
-        mfma_us = w.flops() / (PEAK_FP16_TFLOPS * 1e12) * 1e6
-        if hbm_us >= mfma_us:
-            gbs = w.alg_bytes() / (us * 1e-6) / 1e9
-            rec["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
-                               "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}
-        else:
-            rec["roofline"] = {"bound": "mfma", "achieved": rec["tflops"],
-                               "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
-                               "frac": rec["tflops"] / PEAK_FP16_TFLOPS}
         del cold
         out["cold"] = rec
     if args.path == "fused" and not args.no_workloads:
