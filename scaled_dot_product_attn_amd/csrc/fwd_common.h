@@ -117,7 +117,7 @@ __device__ __forceinline__ void online_softmax(floatx16 s, int lim, float c, flo
 // matrix instructions.
 constexpr float kLazyBound = 256.0f;  // 2^kLazyTau
 static_assert(kLazyTau == 8.0f, "kLazyBound = 2^kLazyTau");
-template <bool MASK, int NB, bool PIPE>
+template <bool MASK, int NB, bool PIPE, int NMF = 8, int NDS = 0>
 __device__ __forceinline__ void softmax_block(floatx16 s, int lim, float c, float& m, float& l,
                                               floatx16* o, half8* pf) {
     if (MASK) {
@@ -149,13 +149,17 @@ __device__ __forceinline__ void softmax_block(floatx16 s, int lim, float c, floa
         pf[h] = __builtin_bit_cast(half8, x);
     }
     if (PIPE) {
-        // interleave the next tile's Q K^T (8 MFMAs, issued by the caller in
-        // this region) with this softmax's vector work
+        // interleave the next tile's Q K^T (NMF MFMAs and the NDS LDS reads
+        // of their operands, issued by the caller in this region) with this
+        // softmax's vector work, the reads running up to four ahead
+        constexpr int pre = NDS < 4 ? NDS : 4;
+        if (pre > 0) __builtin_amdgcn_sched_group_barrier(0x100, pre, 0);  // DS read
         __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < NMF; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+            if (i + pre < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 40 / NMF, 0);  // VALU
         }
     }
     // every weight is at most the lane's sum; the sum is NaN when m = -inf

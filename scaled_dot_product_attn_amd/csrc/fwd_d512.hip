@@ -59,113 +59,184 @@ struct G512 {
     static constexpr int NT = 64 * NW;
     static constexpr int BM = 64;                // query rows per workgroup
     static constexpr int BN = 32;                // keys per tile
-    static constexpr int NS = 2;                 // LDS stages
-    static constexpr int CPR = D / 8;            // 16-byte chunks per row
-    static constexpr int KSTR = D + 8;           // padded K row (halfs)
-    static constexpr int KTILE = BN * KSTR;
-    static constexpr int VTILE = BN * D;
-    static constexpr int STAGE = KTILE + VTILE;
+    static constexpr int NB = DH / 32;           // 32-dim output blocks of a wave
+    static constexpr int TILE = BN * D;          // halfs of a K or V stage (swizzled rows, no pad)
+    static constexpr int ROWS = BN / NW;         // 1 KB rows a wave loads per K (or V) tile
     static constexpr int XCH = NW * 16 * 64;     // floats of the S^T exchange buffer
-    static constexpr int LDS_BYTES = NS * STAGE * 2 + XCH * 4;
-    static constexpr int CH = BN * CPR / NT;     // chunks per thread per K (or V) tile
-    static_assert(CH * NT == BN * CPR, "tile split");
+    // two K stages, two V stages and the exchange buffer
+    static constexpr int LDS_BYTES = 4 * TILE * 2 + XCH * 4;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
+// K row swizzle: 16-byte chunk index XOR (row & 15).  Every 1 KB row starts on
+// the same bank, so without it the 16 rows that a group of 16 lanes reads at
+// one logical chunk would all hit the same four banks.
+__device__ __forceinline__ int swz_k512(int r) { return r & 15; }
 // V row swizzle: XOR chunk bits 2-3 with the row's low two bits, so that the
 // four rows of a transposed read hit different banks.
 __device__ __forceinline__ int swz_v512(int r) { return 4 * (r & 3); }
 
 struct Fwd512 {
     using G = G512;
+    static constexpr int NB = G::NB;
     const _Float16* __restrict__ Q;
     const _Float16* __restrict__ K;
     const _Float16* __restrict__ V;
     _Float16* __restrict__ O;
     float* __restrict__ LSE;
-    _Float16* lds;
-    float* xch;
+    _Float16* lds;  // the workgroup's LDS: K stages, V stages, exchange buffers
     int S;
     bool causal;
     size_t base, lse_base;
     float c;
     uint32_t qsign;
-    int tid, w, lane, g, n, rg, dh;
+    int w, lane, g, n, rg, dh;
     using LdsPtr = __attribute__((address_space(3))) void*;
 
+    // x, opaque to the optimiser: lane-dependent LDS and global offsets
+    // derived from it are recomputed where they are used (a few VALU
+    // instructions) instead of being hoisted out of the key loop, where the
+    // dozens of distinct swizzled offsets would each hold a register.
+    __device__ __forceinline__ static int fresh(int x) {
+        asm volatile("" : "+v"(x));
+        return x;
+    }
+
+    // Stage addresses by arithmetic on the LDS base (no pointer arrays: a
+    // runtime index into one would leave the address space unknown).
+    __device__ __forceinline__ _Float16* ks(int st) const { return lds + st * G::TILE; }
+    __device__ __forceinline__ _Float16* vs(int st) const { return lds + (2 + st) * G::TILE; }
+    __device__ __forceinline__ float* xch() const {
+        return reinterpret_cast<float*>(lds + 4 * G::TILE);
+    }
+
+    // Buffer over key rows j0 .. min(j0 + BN, S) - 1 of t (reads past them
+    // return zero).  j0 is uniform; readfirstlane keeps the descriptor in
+    // scalar registers.
     __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const _Float16* t, int j0) const {
+        j0 = __builtin_amdgcn_readfirstlane(j0);
         return __builtin_amdgcn_make_buffer_rsrc(
             const_cast<_Float16*>(t + base + (size_t)j0 * G::D), (short)0,
-            min(S - j0, G::BN) * G::D * 2, 0x00020000);
+            (S > j0 ? min(S - j0, G::BN) : 0) * G::D * 2, 0x00020000);
     }
-    // Key tile j into LDS stage st, straight from global memory (no staging
-    // registers): one 1 KB load instruction per row (a D = 512 row is 1 KB),
-    // rows 8w .. 8w+7 of K and of V from this wave.  Lane L lands at byte 16 L
-    // of the row: K rows keep their 16-byte pad (M0 = the padded row's
-    // address), V rows are swizzled, so lane L loads the logical chunk the
-    // swizzle puts at physical chunk L.  Rows past S read as zero.  Inline
-    // assembly with M0 = the LDS address, as in the D <= 128 kernel, so the
-    // only waits on these loads are the explicit ones before the barriers.
-    template <bool DO_K = true, bool DO_V = true>
-    __device__ __forceinline__ void dma_tile(int j, int st) const {
-        // uniform by construction; readfirstlane keeps it (and so the buffer
-        // descriptors) in scalar registers where the loop counter lives in a
-        // vector register
-        const int j0 = __builtin_amdgcn_readfirstlane(j * G::BN);
-        const auto rk = tile_rsrc(K, j0), rv = tile_rsrc(V, j0);
-        _Float16* Ks = lds + st * G::STAGE;
-        _Float16* Vs = Ks + G::KTILE;
+    // This wave's ROWS rows of key tile j of t (K when isk, else V) into the
+    // LDS stage dst, straight from global memory: one 1 KB load instruction
+    // per row, lane L landing at byte 16 L of the row and so loading the
+    // logical chunk that the row's swizzle puts there.  Inline assembly with
+    // M0 = the row's LDS address; the only waits on these loads are the
+    // explicit ones before the barriers.
+    __device__ __forceinline__ void dma_row(const __amdgpu_buffer_rsrc_t r, _Float16* dst, int u,
+                                            bool isk, int ln) const {
+        const int row = G::ROWS * w + u;
+        const int logical = ln ^ (isk ? swz_k512(row) : swz_v512(row));
+        const uint32_t m0 = (uint32_t)(uintptr_t)(LdsPtr)(dst + row * G::D);
+        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"((row * G::D + 8 * logical) * 2), "s"(r), "{m0}"(m0)
+                     : "memory");
+    }
+    __device__ __forceinline__ void dma(const _Float16* t, _Float16* dst, int j, bool isk) const {
+        const auto r = tile_rsrc(t, j * G::BN);
+        const int ln = fresh(lane);
 #pragma unroll
-        for (int u = 0; u < G::BN / G::NW; ++u) {
-            const int row = (G::BN / G::NW) * w + u;
-            const uint32_t mk = (uint32_t)(uintptr_t)(LdsPtr)(Ks + row * G::KSTR);
-            if (DO_K) asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                         :
-                         : "v"((row * G::D + 8 * lane) * 2), "s"(rk), "{m0}"(mk)
-                         : "memory");
-            const uint32_t mv = (uint32_t)(uintptr_t)(LdsPtr)(Vs + row * G::D);
-            if (DO_V) asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                         :
-                         : "v"((row * G::D + 8 * (lane ^ swz_v512(row))) * 2), "s"(rv), "{m0}"(mv)
-                         : "memory");
-        }
+        for (int u = 0; u < G::ROWS; ++u) dma_row(r, dst, u, isk, ln);
     }
-    // This wave's tile loads have landed, then the workgroup barrier.
+    // This wave's loads and LDS accesses have landed, then the workgroup barrier.
     __device__ __forceinline__ void barrier_dma() const {
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     }
-
-    // Partial S^T over this wave's 256 head dims: 32 keys x 32 queries.
-    __device__ __forceinline__ floatx16 qk_half(const half8* qf, int st) const {
-        const _Float16* kp = lds + st * G::STAGE + n * G::KSTR + G::DH * dh + 8 * g;
-        floatx16 acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-            half8 kf[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                kf[e] = *reinterpret_cast<const half8*>(kp + 16 * (4 * k4 + e));
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[e], qf[4 * k4 + e], acc, 0, 0, 0);
-        }
-        return acc;
+    // The same, with this wave's last ROWS (= 8) tile-row loads still in
+    // flight (loads complete in issue order).
+    __device__ __forceinline__ void barrier_dma_but8() const {
+        static_assert(G::ROWS == 8, "vmcnt immediate");
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     }
 
-    // O^T (this wave's 256 dims) += V^T P^T for the 32-key tile in stage st.
+    // Partial S^T over this wave's 256 head dims (32 keys x 32 queries) from
+    // K stage st: 16 matrix instructions in two independent accumulation
+    // chains (even and odd 16-dim steps, added at the end), the K fragments
+    // (key n, head dims 256 dh + 16 kk + 8g ..) read a group of four ahead.
+    // With DMA, this wave's 8 rows of key tile jn of K go to K stage dn, one
+    // after every second product, so that the CU's load path is fed evenly
+    // while the matrix cores run.
+    template <bool DMA>
+    __device__ __forceinline__ floatx16 qk_half(const half8* qf, int st, int jn = 0,
+                                                int dn = 0) const {
+        const _Float16* kp = ks(st) + n * G::D;
+        // chunk 32 dh + 2 kk + g = (32 dh + g) | 2 kk (disjoint bits), so the
+        // swizzled chunk is x ^ 2 kk with x = (32 dh + g) ^ swizzle
+        const int x = fresh((32 * dh + g) ^ swz_k512(n));
+        __amdgpu_buffer_rsrc_t r;
+        int ln = 0;
+        if (DMA) {
+            r = tile_rsrc(K, jn * G::BN);
+            ln = fresh(lane);
+        }
+        floatx16 acc[2];
+#pragma unroll
+        for (int r2 = 0; r2 < 16; ++r2) acc[0][r2] = acc[1][r2] = 0.f;
+        half8 kf[2][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            kf[0][e] = *reinterpret_cast<const half8*>(kp + 8 * (x ^ (2 * e)));
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            if (k4 + 1 < 4) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    kf[(k4 + 1) & 1][e] = *reinterpret_cast<const half8*>(
+                        kp + 8 * (x ^ (2 * (4 * (k4 + 1) + e))));
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[e & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[k4 & 1][e], qf[4 * k4 + e],
+                                                                    acc[e & 1], 0, 0, 0);
+                if (DMA && (e & 1)) dma_row(r, ks(dn), 2 * k4 + (e >> 1), true, ln);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return acc[0] + acc[1];
+    }
+    // Publish this wave's partial S^T in exchange buffer x; add the partner's
+    // (same row group, other head-dim half).  Both waves then hold
+    // S_0 + S_1 = S_1 + S_0 bit for bit (fp32 addition commutes).
+    __device__ __forceinline__ void publish(float* x, const floatx16& s) const {
+        float* mine = x + w * 16 * 64;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<float4*>(mine + (4 * q4) * 64 + 4 * lane) =
+                float4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
+    }
+    __device__ __forceinline__ void add_partner(const float* x, floatx16& s) const {
+        const float* other = x + (w ^ 2) * 16 * 64;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 p = *reinterpret_cast<const float4*>(other + (4 * q4) * 64 + 4 * lane);
+            s[4 * q4] += p.x;
+            s[4 * q4 + 1] += p.y;
+            s[4 * q4 + 2] += p.z;
+            s[4 * q4 + 3] += p.w;
+        }
+    }
+
+    // O^T (this wave's 256 dims) += V^T P^T for the 32-key tile in V stage st.
+    template <bool SCHED>
     __device__ __forceinline__ void pv_half(floatx16* o, const half8* pf, int st) const {
-        const _Float16* Vs = lds + st * G::STAGE + G::KTILE;
+        const _Float16* Vs = vs(st);
         const int n16 = n >> 4, jj = n & 15;
         const int sub = (jj & 3) >> 1, half = jj & 1;
         const int sw = swz_v512(jj >> 2);  // (row & 3) == jj >> 2 for every row read
         const _Float16* rowp = Vs + (4 * g + (jj >> 2)) * G::D + 4 * half;
+        // chunk 32 dh + 4 b + 2 n16 + sub = (32 dh + 2 n16 + sub) | 4 b
+        // (disjoint bits): swizzled, x ^ 4 b
+        const int x = fresh((32 * dh + 2 * n16 + sub) ^ sw);
 #pragma unroll
-        for (int b = 0; b < G::DH / 32; ++b) {
-            const _Float16* pb = rowp + 8 * ((32 * dh + 4 * b + 2 * n16 + sub) ^ sw);
+        for (int b = 0; b < NB; ++b) {
+            const _Float16* pb = rowp + 8 * (x ^ (4 * b));
             half8 a[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -182,15 +253,128 @@ struct Fwd512 {
             for (int h = 0; h < 2; ++h)
                 o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[h], pf[h], o[b], 0, 0, 0);
         }
+        if (SCHED) {
+            // the transposed reads of block b+1 ahead of block b's two products
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if (b + 1 < NB) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+            }
+        }
+    }
+
+    // One V^T fragment pair (keys 0-15 and 16-31 of the tile, head dims
+    // 256 dh + 32 b ..) from V stage Vs, for the lane offsets of pv_half.
+    __device__ __forceinline__ void read_v(half8* a, const _Float16* rowp, int x, int b) const {
+        const _Float16* pb = rowp + 8 * (x ^ (4 * b));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            half4 part[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                part[t] = __builtin_bit_cast(
+                    half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                               (lds_half4*)(pb + (16 * h + 8 * t) * G::D)));
+            a[h] = half8{part[0][0], part[0][1], part[0][2], part[0][3],
+                         part[1][0], part[1][1], part[1][2], part[1][3]};
+        }
+    }
+
+    // O^T += V^T P_prev^T for the tile in V stage st, interleaved by hand
+    // with the online softmax of the next score tile s (the lazy-rescale
+    // softmax of softmax_block, same steps and results): block b's two
+    // products go out with the transposed reads of block b+2 and the
+    // weights of registers 2b and 2b+1, so the vector ALUs work while the
+    // matrix cores do.  P of s goes to pn.
+    __device__ __forceinline__ void pv_softmax(floatx16* o, const half8* pf, int st, floatx16 s,
+                                               int lim, float& m, float& l, half8* pn, int jv,
+                                               int dv) const {
+        const _Float16* Vs = vs(st);
+        const int n16 = n >> 4, jj = n & 15;
+        const int sub = (jj & 3) >> 1, half = jj & 1;
+        const int sw = swz_v512(jj >> 2);
+        const _Float16* rowp = Vs + (4 * g + (jj >> 2)) * G::D + 4 * half;
+        const int x = fresh((32 * dh + 2 * n16 + sub) ^ sw);
+        const auto rv = tile_rsrc(V, jv * G::BN);
+        const int ln = fresh(lane);
+        half8 a[3][2];
+        read_v(a[0], rowp, x, 0);
+        read_v(a[1], rowp, x, 1);
+        float q[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (b + 2 < NB) read_v(a[(b + 2) % 3], rowp, x, b + 2);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[b % 3][h], pf[h], o[b], 0, 0, 0);
+            // row b of this wave's share of V tile jv into V stage dv
+            dma_row(rv, vs(dv), b, false, ln);
+#pragma unroll
+            for (int r = 2 * b; r < 2 * b + 2; ++r) {
+                float t = __builtin_fmaf(s[r], c, -m);
+                if ((8 * (r >> 2) + (r & 3)) > lim) t = kNegInf;
+                const float e = __builtin_amdgcn_exp2f(t);
+                q[r & 3] += e;
+                pn[r >> 3][r & 7] = (_Float16)e;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        float psum = (q[0] + q[1]) + (q[2] + q[3]);
+        // every weight is at most the lane's sum; NaN (m = -inf meeting a
+        // masked key) takes the branch too
+        if (__builtin_amdgcn_ballot_w64(!(psum <= kLazyBound)) != 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if ((8 * (r >> 2) + (r & 3)) > lim) s[r] = kNegInf;
+            const float mx = fmaxf(fmaxf(fmaxf(fmaxf(s[0], s[1]), s[2]), fmaxf(fmaxf(s[3], s[4]), s[5])),
+                                   fmaxf(fmaxf(fmaxf(s[6], s[7]), s[8]),
+                                         fmaxf(fmaxf(fmaxf(s[9], s[10]), s[11]),
+                                               fmaxf(fmaxf(fmaxf(s[12], s[13]), s[14]), s[15]))));
+            const float cand = fmaxf(c * max_halves(mx), -kFltMax);
+            const float m_new = fmaxf(m, cand);
+            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+            m = m_new;
+            l *= alpha;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
+            float q2[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float t = __builtin_fmaf(s[r], c, -m);
+                if ((8 * (r >> 2) + (r & 3)) > lim) t = kNegInf;
+                const float e = __builtin_amdgcn_exp2f(t);
+                q2[r & 3] += e;
+                pn[r >> 3][r & 7] = (_Float16)e;
+            }
+            psum = (q2[0] + q2[1]) + (q2[2] + q2[3]);
+        }
+        l += psum;
     }
 
     // Query tile qt over key tiles [kt0, kt1).  part == nullptr: write O and
     // LSE; otherwise leave the partial state in the chunk's workspace slot:
     // unnormalised O as fp32 [64][512], then m[64] (log2 units) and l[64].
+    //
+    // Software pipeline, per key tile i, in two phases with a barrier each:
+    //   P: wait for V(i-1) (K(i+1) may still be in flight), barrier;
+    //      S(i) = own partial + the partner's;
+    //      O += V(i-1)^T P(i-1) on the matrix cores while the vector ALUs
+    //      form P(i) = softmax(S(i)), the loads of V(i) (into V(i-2)'s
+    //      stage) issued between the products
+    //   Q: wait for K(i+1) (V(i) may still be in flight), barrier;
+    //      partial S(i+1) = K(i+1) Q^T, the loads of K(i+2) (into K(i)'s
+    //      stage) issued between the products; publish the partial
+    // and O += V(last)^T P(last) after the loop.  Every tile load has a
+    // phase pair to land; the scores of one tile are live at a time.  The
+    // exchange buffer is written after barrier Q and read after the next
+    // barrier P, always before the writer's next barrier Q: one buffer.
     __device__ void run(int qt, int kt0, int kt1, float* part) {
         const int q0 = qt * G::BM;
         const int row = q0 + 32 * rg + n;
-        const int r_lo = q0 + 32 * rg, r_hi = r_lo + 31;
+        const int vis = causal ? min(row, S - 1) : S - 1;  // last key this lane's row sees
 
         // Q^T fragment of this wave's rows and head-dim half.
         half8 qf[G::DH / 16];
@@ -202,58 +386,67 @@ struct Fwd512 {
                 u32x4 x = src[2 * kk + g];
                 x ^= qsign;
                 qf[kk] = __builtin_bit_cast(half8, x);
+                // held in accumulation registers, which the matrix
+                // instructions read their B operand from directly: the
+                // ordinary registers go to O, the scores and the fragments
+                asm volatile("" : "+a"(qf[kk]));
             }
         }
 
         float m = kNegInf, l = 0.f;
-        floatx16 o[G::DH / 32];
+        floatx16 o[NB];
 #pragma unroll
-        for (int b = 0; b < G::DH / 32; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
 
-        dma_tile(kt0, 0);
+        const int nt = kt1 - kt0;
+        // Tiles whose keys are all in the future of this wave's rows (at most
+        // the last one, for the upper row group of a causal tile) go through
+        // the same steps: every key masked, P = 0, nothing changes.
+
+        // prologue: K(kt0), K(kt0+1); the partial S(kt0)
+        dma(K, ks(0), kt0, true);
+        if (nt > 1) dma(K, ks(1), kt0 + 1, true);
         barrier_dma();
-        float* mine = xch + w * 16 * 64;
-        const float* other = xch + (w ^ 2) * 16 * 64;  // same row group, other half
-        for (int i = kt0; i < kt1; ++i) {
-            const int li = i - kt0;  // LDS stage of tile i: li & 1
-            const int j0 = i * G::BN;
-            // the next tile goes into the stage of tile i-1, which every wave
-            // finished before the last barrier
-            if (i + 1 < kt1) dma_tile<true, false>(i + 1, (li + 1) & 1);
-            const bool skip = causal && j0 > r_hi;  // every key is in this wave's future
-            floatx16 s;
-            if (!skip) {
-                s = qk_half(qf, li & 1);
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    *reinterpret_cast<float4*>(mine + (4 * q4) * 64 + 4 * lane) =
-                        float4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
-            }
-            barrier();  // both sub-tile partials are published
-            if (i + 1 < kt1) dma_tile<false, true>(i + 1, (li + 1) & 1);
-            if (!skip) {
-                // S = S_0 + S_1 in logit space (the same sum in both waves)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const float4 p = *reinterpret_cast<const float4*>(other + (4 * q4) * 64 + 4 * lane);
-                    s[4 * q4] += p.x;
-                    s[4 * q4 + 1] += p.y;
-                    s[4 * q4 + 2] += p.z;
-                    s[4 * q4 + 3] += p.w;
-                }
-                half8 pf[2];
-                const int lim = (causal ? min(row, S - 1) : S - 1) - (j0 + 4 * g);
-                const bool need_mask = (causal && j0 + G::BN - 1 > r_lo) || (j0 + G::BN > S);
-                if (need_mask)
-                    online_softmax<true, G::DH / 32>(s, lim, c, m, l, o, pf);
-                else
-                    online_softmax<false, G::DH / 32>(s, lim, c, m, l, o, pf);
-                pv_half(o, pf, li & 1);
-            }
-            barrier_dma();  // next tile in LDS; exchange buffer free again
+        floatx16 s_cur = qk_half<false>(qf, 0);
+        publish(xch(), s_cur);
+
+        // tile kt0: no P V yet
+        half8 pf[2];
+        barrier_dma();
+        add_partner(xch(), s_cur);
+        dma(V, vs(0), kt0, false);
+        softmax_block<true, NB, false>(s_cur, vis - (kt0 * G::BN + 4 * g), c, m, l, o, pf);
+        if (nt > 1) {
+            barrier_dma_but8();
+            s_cur = nt > 2 ? qk_half<true>(qf, 1, kt0 + 2, 0) : qk_half<false>(qf, 1);
+            publish(xch(), s_cur);
         }
+        for (int li = 1; li < nt; ++li) {
+            const int i = kt0 + li;
+            const int st = li & 1;
+            // phase P
+            if (li + 1 < nt)
+                barrier_dma_but8();
+            else
+                barrier_dma();
+            add_partner(xch(), s_cur);
+            half8 pn[2];
+            pv_softmax(o, pf, st ^ 1, s_cur, vis - (i * G::BN + 4 * g), m, l, pn, i, st);
+            pf[0] = pn[0];
+            pf[1] = pn[1];
+            // phase Q
+            if (li + 1 < nt) {
+                barrier_dma_but8();
+                s_cur = li + 2 < nt ? qk_half<true>(qf, st ^ 1, i + 2, st)
+                                    : qk_half<false>(qf, st ^ 1);
+                publish(xch(), s_cur);
+            }
+        }
+        // the last tile's P V
+        barrier_dma();
+        pv_half<true>(o, pf, (nt - 1) & 1);
 
         // Epilogue: both waves of a row group hold the same m and l; each
         // writes its 256 output dims.
@@ -261,7 +454,7 @@ struct Fwd512 {
         if (part) {
             float* po = part + (size_t)(32 * rg + n) * G::D + G::DH * dh;
 #pragma unroll
-            for (int b = 0; b < G::DH / 32; ++b)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
                     *reinterpret_cast<float4*>(po + 32 * b + 8 * q4 + 4 * g) =
@@ -276,7 +469,7 @@ struct Fwd512 {
         if (row < S) {
             _Float16* orow = O + base + (size_t)row * G::D + G::DH * dh;
 #pragma unroll
-            for (int b = 0; b < G::DH / 32; ++b)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     u32x2 pk;
@@ -335,7 +528,7 @@ fwd512_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
               Chunking ch, int U, float* __restrict__ ws)
 {
     using G = G512;
-    __shared__ __attribute__((aligned(1024))) _Float16 lds[G::NS * G::STAGE + 2 * G::XCH];
+    __shared__ __attribute__((aligned(1024))) _Float16 lds[G::LDS_BYTES / 2];
 
     const int bh = blockIdx.x % BH;
     const int unit = blockIdx.x / BH;
@@ -352,15 +545,13 @@ fwd512_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     f.O = O;
     f.LSE = LSE;
     f.lds = lds;
-    f.xch = reinterpret_cast<float*>(lds + G::NS * G::STAGE);
     f.S = S;
     f.causal = causal != 0;
     f.base = (size_t)bh * S * G::D;
     f.lse_base = (size_t)bh * S;
     f.c = c;
     f.qsign = qsign;
-    f.tid = threadIdx.x;
-    f.w = threadIdx.x >> 6;
+    f.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     f.lane = threadIdx.x & 63;
     f.g = f.lane >> 5;
     f.n = f.lane & 31;
