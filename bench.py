@@ -487,7 +487,11 @@ def main():
     roof = binding_roof(flops, nbytes, step_us)
     roof["traffic"] = measured_traffic(w.name, args.path)
     roof["launch_us"] = step_us
-    roof["launches_per_step"] = {"fused": 1, "unfused": 3, "splitkv": 2, "decode": 1 if not decode or
+    roof["launches_per_step"] = {"fused": 1, "unfused": 3,
+                                 "splitkv": 1 if args.path != "splitkv" or
+                                 attn.splitkv_workspace_bytes(w.B, w.H, w.S, w.D, w.causal,
+                                                              args.splits) == 0 else 2,
+                                 "decode": 1 if not decode or
                                  attn.decode_workspace_bytes(w.B, w.H, w.Sq, w.Sk, w.D, w.causal,
                                                              dsplits) == 0 else 2,
                                  "bwd": 2}[args.path]

@@ -108,9 +108,11 @@ int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o,
                      void* stream);
 
 /*
- * Split-KV forward for head dimension 512, for shapes with few (batch, head)
- * slices and long causal rows, where one workgroup per query tile leaves most
- * of the GPU idle.  The key range of every 64-row query tile is cut into
+ * Split-KV forward, for shapes with few (batch, head) slices and long causal
+ * rows, where one workgroup per query tile leaves most of the GPU idle.
+ * D = 64 or 128: the decode kernel below with Sq = Sk = S (same arguments,
+ * workspace and results as attn_fwd_decode; its chunks are 64-key tiles).
+ * D = 512: the key range of every 64-row query tile is cut into
  * chunks of at most C = ceil(ceil(S/32) / splits) 32-key tiles; each chunk is
  * one workgroup that leaves its partial state (unnormalised O in fp32, row
  * max and row sum) in `workspace`, and a second kernel merges the chunks of
@@ -122,7 +124,7 @@ int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o,
  * "Experiment one: ten mappings, forty handwritten kernels") says must be
  * paid.  Query tiles with a single chunk are written directly; splits = 1
  * gives the fused result bit for bit.
- *   D         : must be 512 (else ATTN_ERR_HEAD_DIM)
+ *   D         : 64, 128 or 512 (else ATTN_ERR_HEAD_DIM)
  *   splits    : >= 1 (else ATTN_ERR_SPLITS)
  *   workspace : device memory of at least
  *               attn_fwd_splitkv_workspace_bytes(B, H, S, D, causal, splits)

@@ -186,14 +186,18 @@ def splitkv_workspace_bytes(B: int, H: int, S: int, D: int, causal: bool, splits
                                                                 splits))
 
 
-def splitkv_splits(B: int, H: int, S: int, causal: bool, max_units: int = 282) -> int:
-    """A default split count for fwd_splitkv: the largest one (up to 16) whose
-    (batch, head, query tile, chunk) work units still run in about one wave on
-    the 256 CUs of an MI355X (one workgroup per CU, 10% over allowed).  A
-    query tile of 64 rows sees nkt 32-key tiles (all ceil(S/32), or those up
-    to its last row when causal) and is cut into ceil(nkt / C) chunks,
+def splitkv_splits(B: int, H: int, S: int, causal: bool, max_units: int = 282,
+                   D: int = 512) -> int:
+    """A default split count for fwd_splitkv.  D = 64, 128: decode_splits
+    with Sq = Sk = S.  D = 512: the largest count (up to 16) whose (batch,
+    head, query tile, chunk) work units still run in about one wave on the
+    256 CUs of an MI355X (one workgroup per CU, 10% over allowed).  A query
+    tile of 64 rows sees nkt 32-key tiles (all ceil(S/32), or those up to its
+    last row when causal) and is cut into ceil(nkt / C) chunks,
     C = ceil(ceil(S/32) / splits).  At B1 H8 S1024 causal it picks 3 (256
     units), measured faster than 2 (192 units) and 4 (320 units)."""
+    if D in (64, 128):
+        return decode_splits(B, H, S, S)
     nmax = -(-S // 32)
     tq = -(-S // 64)
     best = 1
@@ -210,15 +214,16 @@ def splitkv_splits(B: int, H: int, S: int, causal: bool, max_units: int = 282) -
 
 def fwd_splitkv(q, k, v, *, causal: bool, splits: int | None = None, scale: float | None = None,
                 out=None, lse=None, workspace=None):
-    """Split-KV forward (D = 512): every query tile's key range in chunks of
-    at most ceil(ceil(S/32) / splits) 32-key tiles, merged in chunk order.
-    ``splits`` defaults to splitkv_splits(B, H, S, causal).
+    """Split-KV forward: every query tile's key range in chunks (D = 512: of
+    at most ceil(ceil(S/32) / splits) 32-key tiles; D = 64, 128: the decode
+    kernel with Sq = Sk, 64-key tiles), merged in chunk order.
+    ``splits`` defaults to splitkv_splits(B, H, S, causal, D=D).
     ``workspace``: a uint8 GPU tensor of at least splitkv_workspace_bytes(...)
     bytes; allocated with torch when not given and needed."""
     L = load_library()
     B, H, S, D, out, lse, scale, stream = _prepare(q, k, v, out, lse, scale)
     if splits is None:
-        splits = splitkv_splits(B, H, S, causal)
+        splits = splitkv_splits(B, H, S, causal, D=D)
     wptr, wbytes = _workspace(workspace, splitkv_workspace_bytes(B, H, S, D, causal, splits),
                               q.device)
     _check(L.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),

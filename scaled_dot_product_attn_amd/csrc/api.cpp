@@ -118,6 +118,9 @@ int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o,
 }
 
 size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int S, int D, int causal, int splits) {
+    // D = 64, 128: the decode kernel with Sq = Sk = S (its bottom-right causal
+    // alignment is then attn_fwd's)
+    if (D == 64 || D == 128) return attn_fwd_decode_workspace_bytes(B, H, S, S, D, causal, splits);
     if (B < 1 || H < 1 || S < 1 || D != 512 || splits < 1) return 0;
     const int T = (S + 63) / 64;
     if (attn::splitkv_d512_units(S, causal != 0, splits) == T) return 0;  // nothing is split
@@ -127,6 +130,9 @@ size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int S, int D, int causal, 
 int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int H, int S, int D, int causal, float scale, int splits,
                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (D == 64 || D == 128)
+        return attn_fwd_decode(q, k, v, o, lse, B, H, S, S, D, causal, scale, splits, workspace,
+                               workspace_bytes, stream);
     const int st = validate(q, k, v, o, lse, B, H, S, D, scale);
     if (st != ATTN_OK) return st;
     if (D != 512) return ATTN_ERR_HEAD_DIM;

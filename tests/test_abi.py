@@ -128,7 +128,10 @@ def test_splitkv_workspace_bytes(L, S, causal, splits):
 
 
 def test_splitkv_validation(L):
-    assert L.attn_fwd_splitkv_workspace_bytes(1, 8, 1024, 128, 1, 4) == 0
+    # D = 64, 128: the decode kernel with Sq = Sk, same workspace
+    for D in (64, 128):
+        n = L.attn_fwd_splitkv_workspace_bytes(1, 8, 1024, D, 1, 4)
+        assert n > 0 and n == L.attn_fwd_decode_workspace_bytes(1, 8, 1024, 1024, D, 1, 4)
     assert L.attn_fwd_splitkv_workspace_bytes(1, 8, 1024, 512, 1, 0) == 0
     need = L.attn_fwd_splitkv_workspace_bytes(1, 2, 1024, 512, 1, 4)
     assert need > 0
@@ -138,8 +141,12 @@ def test_splitkv_validation(L):
     assert L.attn_fwd_splitkv(*args, 4, W, need - 1, None) == C["ATTN_ERR_WORKSPACE"]
     assert L.attn_fwd_splitkv(*args, 4, Q, need, None) == C["ATTN_ERR_ALIAS"]
     assert L.attn_fwd_splitkv(*args, 0, W, need, None) == C["ATTN_ERR_SPLITS"]
+    d96 = (Q, K, V, O, LSE, 1, 2, 1024, 96, 1, 0.1)
+    assert L.attn_fwd_splitkv(*d96, 4, W, need, None) == C["ATTN_ERR_HEAD_DIM"]
     d128 = (Q, K, V, O, LSE, 1, 2, 1024, 128, 1, 0.1)
-    assert L.attn_fwd_splitkv(*d128, 4, W, need, None) == C["ATTN_ERR_HEAD_DIM"]
+    need128 = L.attn_fwd_splitkv_workspace_bytes(1, 2, 1024, 128, 1, 4)
+    assert L.attn_fwd_splitkv(*d128, 4, W, need128 - 1, None) == C["ATTN_ERR_WORKSPACE"]
+    assert L.attn_fwd_splitkv(*d128, 0, W, need128, None) == C["ATTN_ERR_SPLITS"]
     nul = (None, K, V, O, LSE, 1, 2, 1024, 512, 1, 0.1)
     assert L.attn_fwd_splitkv(*nul, 4, W, need, None) == C["ATTN_ERR_NULL"]
 
