@@ -106,6 +106,9 @@ int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o,
                      void* stream) {
     const int st = validate(q, k, v, o, lse, B, H, S, D, scale);
     if (st != ATTN_OK) return st;
+    // the Q K^T kernel's grid: (batch, head, 64-row query tile, chunk of 4 key tiles)
+    const long long tq = (S + 63) / 64;
+    if ((long long)B * H * tq * ((tq + 3) / 4) > INT32_MAX) return ATTN_ERR_SHAPE;
     const size_t need = attn_fwd_unfused_workspace_bytes(B, H, S);
     if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     const size_t nt = (size_t)B * H * S * D * 2, nl = (size_t)B * H * S * 4;

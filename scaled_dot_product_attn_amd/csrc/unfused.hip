@@ -37,51 +37,110 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 
 // ---------------------------------------------------------------- Q K^T
 
-// One workgroup = 64 queries x 64 keys; wave (wq, wk) a 32 x 32 block.
-// DC head dims starting at d0 are reduced; ACC adds into S instead of writing.
+// One workgroup per (batch, head, 64-row query tile, chunk of up to kQkChunk
+// 64-key tiles), the heaviest query tiles first under causal masking, walking
+// the key tiles of its chunk that the tile's rows see.  Wave
+// (wq, wk): query rows 32wq .. +31 against keys 32wk .. +31 of every key
+// tile.  Its Q fragments stay in registers and the next tile's K fragments
+// are loaded while the current tile's products and stores run, so the
+// kernel streams S out instead of waiting on a load per 64 x 64 block.
+// DC head dims starting at d0 are reduced; ACC adds into S instead of
+// writing.  Under causal masking only the blocks holding some j <= i are
+// stored (the softmax reads no other entry).
+constexpr int kQkChunk = 4;
+
 template <int DC, bool ACC>
 __global__ void __launch_bounds__(256)
 qk_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
-          float* __restrict__ Sm, int S, int Sp, int D, int d0, int causal, float scale)
+          float* __restrict__ Sm, int BH, int S, int Sp, int D, int d0, int causal, float scale)
 {
+    constexpr int NK = DC / 16;
     const int TQ = (S + 63) / 64;
-    const int kt = blockIdx.x;
-    const int bh = blockIdx.y / TQ, qt = blockIdx.y % TQ;
-    if (causal && kt > qt) return;  // every key of the block is in the future
+    const int NC = (TQ + kQkChunk - 1) / kQkChunk;  // chunks of the longest row
+    const int bh = blockIdx.x % BH;
+    const int u = blockIdx.x / BH;
+    const int qt = causal ? TQ - 1 - u / NC : u / NC;
+    const int kc = u % NC;
+    const int kend = causal ? qt + 1 : TQ;        // key tiles the rows see
+    const int kt0 = kc * kQkChunk;
+    if (kt0 >= kend) return;                      // a chunk past the diagonal
+    const int nkt = min(kend - kt0, kQkChunk);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int g = lane >> 5, n = lane & 31;
     const int wq = w & 1, wk = w >> 1;
     const size_t base = (size_t)bh * S * D;
     const int qrow = min(qt * 64 + 32 * wq + n, S - 1);  // A operand row (query)
-    const int krow = min(kt * 64 + 32 * wk + n, S - 1);  // B operand column (key)
-    const _Float16* qp = Q + base + (size_t)qrow * D + d0 + 8 * g;
-    const _Float16* kp = K + base + (size_t)krow * D + d0 + 8 * g;
-    floatx16 acc;
+    half8 qf[NK];
+    {
+        const _Float16* qp = Q + base + (size_t)qrow * D + d0 + 8 * g;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll 4
-    for (int kk = 0; kk < DC / 16; ++kk) {
-        const half8 a = *reinterpret_cast<const half8*>(qp + 16 * kk);
-        const half8 b = *reinterpret_cast<const half8*>(kp + 16 * kk);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+        for (int kk = 0; kk < NK; ++kk) qf[kk] = *reinterpret_cast<const half8*>(qp + 16 * kk);
     }
-    // C[m = query][n = key]: register r holds query 8(r/4) + 4g + r%4, key n
-    const int j = kt * 64 + 32 * wk + n;
-    if (j >= S) return;
+    // B operand column (key) fragments of key tile t
+    auto load_k = [&](int t, half8* kf) {
+        const int krow = min(t * 64 + 32 * wk + n, S - 1);
+        const _Float16* kp = K + base + (size_t)krow * D + d0 + 8 * g;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int i = qt * 64 + 32 * wq + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (i < S) {
-            float* dst = Sm + ((size_t)bh * S + i) * Sp + j;
-            const float v = scale * acc[r];
-            *dst = ACC ? *dst + v : v;
+        for (int kk = 0; kk < NK; ++kk) kf[kk] = *reinterpret_cast<const half8*>(kp + 16 * kk);
+    };
+    const int i0 = qt * 64 + 32 * wq;  // first query row of the wave
+    // the wave's 32 x 32 fp32 block goes out through LDS, so that every
+    // store writes whole 128-byte row pieces: 16-byte lanes, 8 rows per
+    // instruction
+    __shared__ __attribute__((aligned(16))) float tb[4][32 * 32];
+    float* mine = tb[w];
+    auto block = [&](int t, const half8* kf) {
+        floatx16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qf[kk], kf[kk], acc, 0, 0, 0);
+        const int k0 = t * 64 + 32 * wk;
+        if (causal && k0 > i0 + 31) return;  // every key past every row (uniform)
+        // C[m = query][n = key]: register r holds query 8(r/4) + 4g + r%4, key n
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine[(8 * (r >> 2) + 4 * g + (r & 3)) * 32 + n] = scale * acc[r];
+        __builtin_amdgcn_wave_barrier();
+        wait_lgkm0();
+        // lane L: row L / 8 + 8 s of the block, columns 4 (L % 8) .. +3
+        const int c4 = 4 * (lane & 7);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const int rr = (lane >> 3) + 8 * s4;
+            float4 v = *reinterpret_cast<const float4*>(mine + rr * 32 + c4);
+            const int i = i0 + rr, j = k0 + c4;
+            // Sp is a multiple of 64 and j of 4: the 4 columns lie in the row
+            // (past S they are padding that no kernel reads)
+            if (i < S && j < Sp) {
+                float4* dst = reinterpret_cast<float4*>(Sm + ((size_t)bh * S + i) * Sp + j);
+                if (ACC) {
+                    const float4 a = *dst;
+                    v.x += a.x, v.y += a.y, v.z += a.z, v.w += a.w;
+                }
+                *dst = v;
+            }
         }
+        // the block's LDS reads are done before the next block's writes
+        wait_lgkm0();
+        __builtin_amdgcn_wave_barrier();
+    };
+    half8 ka[NK], kb[NK];
+    load_k(kt0, ka);
+    for (int t = kt0; t < kt0 + nkt; t += 2) {
+        if (t + 1 < kt0 + nkt) load_k(t + 1, kb);
+        block(t, ka);
+        if (t + 1 >= kt0 + nkt) break;
+        if (t + 2 < kt0 + nkt) load_k(t + 2, ka);
+        block(t + 1, kb);
     }
 }
 
 // ---------------------------------------------------------------- softmax
 
-// One wave per row; 4 rows per workgroup.
+// One wave per row, 4 rows per workgroup: 16-byte loads (a row of S is
+// 256-byte aligned, Sp being a multiple of 64), a pass for the row max and
+// sum, a second for P (the row is then in L2), 8-byte P stores.
 __global__ void __launch_bounds__(256)
 softmax_kernel(const float* __restrict__ Sm, _Float16* __restrict__ P, float* __restrict__ LSE,
                int BHS, int S, int Sp, int causal)
@@ -95,14 +154,26 @@ softmax_kernel(const float* __restrict__ Sm, _Float16* __restrict__ P, float* __
     // of its query block (at most 128 rows), so past the diagonal write zeros
     // up to the next multiple of 128.
     const int Lp = causal ? min(Sp, ((i + 128) / 128) * 128) : Sp;
-    const float* srow = Sm + (size_t)rowid * Sp;
+    const float4* srow = reinterpret_cast<const float4*>(Sm + (size_t)rowid * Sp);
     _Float16* prow = P + (size_t)rowid * Sp;
-    // per-lane running max and sum (base-2), then a wave reduction
+    // per-lane running max and sum (base-2) over 4-column groups, then a
+    // wave reduction
     float m = kNegInf, l = 0.f;
-    for (int j = lane; j < L; j += 64) {
-        const float x = srow[j] * kLog2e;
-        const float mn = fmaxf(m, x);
-        l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(x - mn);
+#pragma unroll 4
+    for (int j4 = lane; 4 * j4 < L; j4 += 64) {
+        const float4 x4 = srow[j4];
+        float x[4] = {x4.x, x4.y, x4.z, x4.w};
+        float mx = kNegInf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = 4 * j4 + e < L ? x[e] * kLog2e : kNegInf;
+            mx = fmaxf(mx, x[e]);
+        }
+        const float mn = fmaxf(m, mx);
+        float add = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) add += __builtin_amdgcn_exp2f(x[e] - mn);
+        l = l * __builtin_amdgcn_exp2f(m - mn) + add;
         m = mn;
     }
 #pragma unroll
@@ -114,9 +185,23 @@ softmax_kernel(const float* __restrict__ Sm, _Float16* __restrict__ P, float* __
         m = mn;
     }
     const float inv = 1.0f / l;
-    for (int j = lane; j < Lp; j += 64) {
-        const float p = j < L ? __builtin_amdgcn_exp2f(srow[j] * kLog2e - m) * inv : 0.f;
-        prow[j] = (_Float16)p;
+#pragma unroll 4
+    for (int j4 = lane; 4 * j4 < Lp; j4 += 64) {
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+        if (4 * j4 < L) {
+            const float4 x4 = srow[j4];
+            x[0] = x4.x, x[1] = x4.y, x[2] = x4.z, x[3] = x4.w;
+        }
+        u32x2 pk;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int j = 4 * j4 + 2 * h;
+            const float p0 = j < L ? __builtin_amdgcn_exp2f(x[2 * h] * kLog2e - m) * inv : 0.f;
+            const float p1 = j + 1 < L ? __builtin_amdgcn_exp2f(x[2 * h + 1] * kLog2e - m) * inv : 0.f;
+            pk[h] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)p0) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)p1) << 16);
+        }
+        *reinterpret_cast<u32x2*>(prow + 4 * j4) = pk;
     }
     if (lane == 0) LSE[rowid] = (m + __builtin_amdgcn_logf(l)) * kLn2;
 }
@@ -185,18 +270,29 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
     const int n16 = n >> 4, jj = n & 15;
     const int sub = (jj & 3) >> 1, half = jj & 1;
     const int sw = swz_pv<D>(jj >> 2);  // (row & 3) == jj >> 2 for every row read
+    // P^T operands of a key tile: this lane's query, keys j0 + 16ks + 8g .. +7,
+    // loaded a tile ahead of their products
+    half8 pcur[G::BN / 16], pnext[G::BN / 16];
+    auto load_p = [&](int t, half8* pf) {
+#pragma unroll
+        for (int ks = 0; ks < G::BN / 16; ++ks)
+            pf[ks] = *reinterpret_cast<const half8*>(prow + t * G::BN + 16 * ks);
+    };
     load(0);
+    load_p(0, pcur);
     for (int t = 0; t < nT; ++t) {
         store();
         barrier();
-        if (t + 1 < nT) load(t + 1);
+        if (t + 1 < nT) {
+            load(t + 1);
+            load_p(t + 1, pnext);
+        }
         // transposed reads deliver keys 16ks + 8g + 4tt + 0..3: the lane's 8 keys
         // are contiguous, matching a 16-byte load of its P row
         const _Float16* rowp = vs + (8 * g + (jj >> 2)) * D + 4 * half;
 #pragma unroll
         for (int ks = 0; ks < G::BN / 16; ++ks) {
-            // P^T operand: this lane's query, keys j0 + 16ks + 8g .. +7
-            const half8 pf = *reinterpret_cast<const half8*>(prow + t * G::BN + 16 * ks);
+            const half8 pf = pcur[ks];
 #pragma unroll
             for (int b = 0; b < G::DW / 32; ++b) {
                 const int logical = (G::DW * dq) / 8 + 4 * b + 2 * n16 + sub;
@@ -212,6 +308,8 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
             }
         }
         barrier();
+#pragma unroll
+        for (int ks = 0; ks < G::BN / 16; ++ks) pcur[ks] = pnext[ks];
     }
     if (qrow < S) {
         _Float16* orow = O + vbase + (size_t)qrow * D + G::DW * dq;
@@ -252,18 +350,18 @@ hipError_t launch_unfused(const FwdArgs& a, void* workspace) {
     float* Sm = reinterpret_cast<float*>(workspace);
     _Float16* P = reinterpret_cast<_Float16*>(Sm + (size_t)BH * S * Sp);
     const int TQ = (S + 63) / 64;
-    const dim3 qk_grid((unsigned)TQ, (unsigned)(BH * TQ));
+    const dim3 qk_grid((unsigned)(BH * TQ * ((TQ + kQkChunk - 1) / kQkChunk)));
     const hipStream_t st = (hipStream_t)a.stream;
     const _Float16* q = (const _Float16*)a.q;
     const _Float16* k = (const _Float16*)a.k;
     if (a.D == 64)
-        hipLaunchKernelGGL((qk_kernel<64, false>), qk_grid, dim3(256), 0, st, q, k, Sm, S, Sp, 64, 0, a.causal, a.scale);
+        hipLaunchKernelGGL((qk_kernel<64, false>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 64, 0, a.causal, a.scale);
     else if (a.D == 128)
-        hipLaunchKernelGGL((qk_kernel<128, false>), qk_grid, dim3(256), 0, st, q, k, Sm, S, Sp, 128, 0, a.causal, a.scale);
+        hipLaunchKernelGGL((qk_kernel<128, false>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 128, 0, a.causal, a.scale);
     else {
         // two head-dim sub-tiles, summed into S before the softmax
-        hipLaunchKernelGGL((qk_kernel<256, false>), qk_grid, dim3(256), 0, st, q, k, Sm, S, Sp, 512, 0, a.causal, a.scale);
-        hipLaunchKernelGGL((qk_kernel<256, true>), qk_grid, dim3(256), 0, st, q, k, Sm, S, Sp, 512, 256, a.causal, a.scale);
+        hipLaunchKernelGGL((qk_kernel<256, false>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 512, 0, a.causal, a.scale);
+        hipLaunchKernelGGL((qk_kernel<256, true>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 512, 256, a.causal, a.scale);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
