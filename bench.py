@@ -561,7 +561,7 @@ def main():
 
             def wstep(i, wc=wc, qc=qc, kc=kc, vc=vc, oc=oc, lc=lc):
                 attn.fwd(qc, kc, vc, causal=wc.causal, scale=wc.scale, out=oc, lse=lc)
-            recs.append(fused_record(wc, replay_us(wstep, 100, dev, stream)))
+            recs.append(fused_record(wc, replay_us(wstep, 300, dev, stream)))
             del qc, kc, vc, oc, lc
         out["workloads"] = recs
     if not args.no_cpu_baseline and args.path == "bwd":
