@@ -396,7 +396,7 @@ def main():
                                                     1.0)).to(dev)
             fw.append((of, lf, do))
         grads = tuple(torch.empty(w.shape, dtype=torch.float16, device=dev) for _ in range(3))
-        ws = torch.empty(attn.bwd_workspace_bytes(w.B, w.H, w.S), dtype=torch.uint8,
+        ws = torch.empty(attn.bwd_workspace_bytes(w.B, w.H, w.S, w.D), dtype=torch.uint8,
                          device=dev)
 
     def step(i):
@@ -494,7 +494,7 @@ def main():
                                  "decode": 1 if not decode or
                                  attn.decode_workspace_bytes(w.B, w.H, w.Sq, w.Sk, w.D, w.causal,
                                                              dsplits) == 0 else 2,
-                                 "bwd": 2}[args.path]
+                                 "bwd": 9 if w.D == 512 else 2}[args.path]
     roof["per_launch"] = {"flops": flops, "alg_bytes": nbytes}
 
     out = {

@@ -188,7 +188,7 @@ int attn_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o
                             int splits, void* stream);
 
 /*
- * Backward of attn_fwd for D = 64 or 128: the gradients of L = sum(dO * O)
+ * Backward of attn_fwd for D = 64, 128 or 512: the gradients of L = sum(dO * O)
  * with respect to q, k and v ("Validating Memory-Optimal Transformer Kernels
  * on Real Hardware", abstract and section 4, which measures this backward and
  * its atomic-free rewrite):
@@ -203,15 +203,23 @@ int attn_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o
  *   dq, dk, dv       : fp16 [B, H, S, D], device, written; they must not
  *                      overlap each other or any input
  *   workspace        : device memory of at least
- *                      attn_bwd_workspace_bytes(B, H, S) bytes (one float
- *                      per row), owned by the caller and overwritten
+ *                      attn_bwd_workspace_bytes_d(B, H, S, D) bytes, owned
+ *                      by the caller and overwritten: for D = 64, 128 one
+ *                      float per row (= attn_bwd_workspace_bytes(B, H, S));
+ *                      for D = 512 the materialised intermediates,
+ *                      B H (14 S Sp + 4 S) bytes with Sp = S rounded up to 64
  * Accumulation is fp32; P and dS are rounded to fp16 before the products
- * that consume them.  Two launches on `stream`, asynchronous like
- * attn_fwd; no atomics, so the outputs are deterministic.  Returns the same
- * status codes as attn_fwd (ATTN_ERR_HEAD_DIM for D other than 64 or 128,
+ * that consume them.  No atomics, so the outputs are deterministic.
+ * D = 64, 128: two launches (P recomputed, never stored).  D = 512: the
+ * n x n scores and score gradients (S, dP in fp32; dS, P^T, dS^T in fp16)
+ * are stored in the workspace and re-read by MFMA products, nine launches
+ * (the same section of the paper measures this storing trade).  All on
+ * `stream`, asynchronous like attn_fwd.  Returns the same status codes as
+ * attn_fwd (ATTN_ERR_HEAD_DIM for D other than 64, 128 or 512,
  * ATTN_ERR_WORKSPACE for a missing or short workspace).
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int S);
+size_t attn_bwd_workspace_bytes_d(int B, int H, int S, int D);
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dout, void* dq, void* dk, void* dv, int B, int H, int S, int D,
              int causal, float scale, void* workspace, size_t workspace_bytes, void* stream);

@@ -22,7 +22,7 @@ __all__ = ["AttnError", "fwd", "fwd_unfused", "unfused_workspace_bytes", "fwd_sp
 SYMBOLS = ("attn_fwd", "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
            "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
            "attn_fwd_decode", "attn_fwd_decode_workspace_bytes", "attn_fwd_decode_noalloc",
-           "attn_bwd", "attn_bwd_workspace_bytes",
+           "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_workspace_bytes_d",
            "attn_head_dim_supported", "attn_status_string", "attn_last_hip_error")
 
 ATTN_ERR_LAUNCH = -5
@@ -78,6 +78,8 @@ def load_library(path: str = LIB_PATH):
     L.attn_bwd.restype = I
     L.attn_bwd_workspace_bytes.argtypes = [I, I, I]
     L.attn_bwd_workspace_bytes.restype = Z
+    L.attn_bwd_workspace_bytes_d.argtypes = [I, I, I, I]
+    L.attn_bwd_workspace_bytes_d.restype = Z
     L.attn_head_dim_supported.argtypes = [I]
     L.attn_head_dim_supported.restype = I
     L.attn_status_string.argtypes = [I]
@@ -318,13 +320,13 @@ def fwd_decode_noalloc(q, k, v, *, causal: bool, splits: int | None = None,
     return out, lse
 
 
-def bwd_workspace_bytes(B: int, H: int, S: int) -> int:
-    return int(load_library().attn_bwd_workspace_bytes(B, H, S))
+def bwd_workspace_bytes(B: int, H: int, S: int, D: int = 128) -> int:
+    return int(load_library().attn_bwd_workspace_bytes_d(B, H, S, D))
 
 
 def bwd(q, k, v, o, lse, do, *, causal: bool, scale: float | None = None, dq=None, dk=None,
         dv=None, workspace=None):
-    """Backward of fwd (D = 64 or 128): q, k, v, o, do contiguous fp16
+    """Backward of fwd (D = 64, 128 or 512): q, k, v, o, do contiguous fp16
     [B, H, S, D] and lse fp32 [B, H, S] on one GPU, o and lse from fwd with the
     same causal and scale.  Returns (dq, dk, dv), fp16 [B, H, S, D].
     Enqueued on the current stream; asynchronous."""
@@ -342,7 +344,7 @@ def bwd(q, k, v, o, lse, do, *, causal: bool, scale: float | None = None, dq=Non
             raise ValueError(f"{name} must be a contiguous float16 tensor shaped like q")
         grads.append(t)
     L = load_library()
-    wptr, wbytes = _workspace(workspace, bwd_workspace_bytes(B, H, S), q.device)
+    wptr, wbytes = _workspace(workspace, bwd_workspace_bytes(B, H, S, D), q.device)
     _check(L.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                       do.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
                       grads[2].data_ptr(), B, H, S, D, int(bool(causal)), scale,

@@ -206,6 +206,14 @@ size_t attn_bwd_workspace_bytes(int B, int H, int S) {
     return (size_t)B * H * S * sizeof(float);  // dO . O per row
 }
 
+size_t attn_bwd_workspace_bytes_d(int B, int H, int S, int D) {
+    if (D == 512) {
+        if (B < 1 || H < 1 || S < 1) return 0;
+        return attn::bwd512_workspace_bytes(B, H, S);
+    }
+    return attn_bwd_workspace_bytes(B, H, S);
+}
+
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dout, void* dq, void* dk, void* dv, int B, int H, int S, int D,
              int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
@@ -216,9 +224,15 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     if (bh > INT32_MAX || (long long)S > INT32_MAX / 2 || bh * S > INT32_MAX / 2 ||
         bh * ((S + 63) / 64) > INT32_MAX || (long long)S * D * 2 >= kMaxSliceBytes)
         return ATTN_ERR_SHAPE;
-    if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+    if (D != 64 && D != 128 && D != 512) return ATTN_ERR_HEAD_DIM;
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
-    const size_t need = attn_bwd_workspace_bytes(B, H, S);
+    if (D == 512) {
+        // the materialised form's grids: Q K^T (query tile, 4-key-tile chunk)
+        // and the dS pass (query tile, key tile), per (batch, head)
+        const long long tq = (S + 63) / 64;
+        if (bh * tq * tq > INT32_MAX) return ATTN_ERR_SHAPE;
+    }
+    const size_t need = attn_bwd_workspace_bytes_d(B, H, S, D);
     if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     const size_t nt = (size_t)bh * S * D * 2, nl = (size_t)bh * S * 4;
     const void* in[7] = {q, k, v, o, dout, lse, workspace};
@@ -234,7 +248,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
         if (overlaps(workspace, need, in[j], in_n[j])) return ATTN_ERR_ALIAS;
     const attn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, B, H, S, D,
                           causal != 0, scale, workspace, stream};
-    return launched(attn::launch_bwd(a));
+    return launched(D == 512 ? attn::launch_bwd512(a) : attn::launch_bwd(a));
 }
 
 const char* attn_status_string(int status) {

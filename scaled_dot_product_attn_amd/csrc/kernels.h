@@ -85,5 +85,9 @@ struct BwdArgs {
     void* stream;
 };
 hipError_t launch_bwd(const BwdArgs& a);
+// Backward, D = 512, with S, dP, dS, P^T and dS^T materialised in `workspace`
+// (bwd512_workspace_bytes), built from the unfused ablation's kernels.
+size_t bwd512_workspace_bytes(int B, int H, int S);
+hipError_t launch_bwd512(const BwdArgs& a);
 
 }  // namespace attn

@@ -340,6 +340,125 @@ hipError_t launch_pv(const FwdArgs& a, const _Float16* P, int Sp) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- backward, D = 512
+//
+// The D <= 128 backward (bwd_dq.hip, bwd_dkdv.hip) keeps a key tile's K and V
+// rows and its dK, dV accumulators in registers; at D = 512 those alone are
+// four times the register file of a wave.  The D = 512 backward instead
+// materialises the n x n intermediates, with the ablation's kernels:
+//   S  = scale Q K^T, dP = dO V^T      qk_kernel, two 256-wide passes each (fp32)
+//   Dlt = rowsum(dO * O)               bwd512_delta_kernel
+//   P = exp(S - LSE), dS = scale P (dP - Dlt)   bwd512_ds_kernel: dS, and P^T,
+//                                      dS^T transposed through LDS (fp16)
+//   dV = P^T dO, dK = dS^T Q, dQ = dS K         pv_kernel
+// the storing-and-re-reading trade that "Validating Memory-Optimal Transformer
+// Kernels on Real Hardware" (section 4) measures against atomics: no atomics,
+// deterministic, and the n x n traffic paid in HBM.
+
+// Dlt[row] = dO_row . O_row (fp32), one wave per row, 8 dims per lane.
+__global__ void __launch_bounds__(256)
+bwd512_delta_kernel(const _Float16* __restrict__ dO, const _Float16* __restrict__ O,
+                    float* __restrict__ dlt, int BHS)
+{
+    const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= BHS) return;
+    const int lane = threadIdx.x & 63;
+    const half8 a = *reinterpret_cast<const half8*>(dO + (size_t)row * 512 + 8 * lane);
+    const half8 b = *reinterpret_cast<const half8*>(O + (size_t)row * 512 + 8 * lane);
+    float x = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x = __builtin_fmaf((float)a[e], (float)b[e], x);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    if (lane == 0) dlt[row] = x;
+}
+
+// One workgroup per 64 x 64 tile (query block bi, key block bj) of a (batch,
+// head), every tile of the S x Sp matrices (tiles past the causal diagonal
+// and columns past S write zeros): P = exp(S - LSE) where key j is visible
+// to query i, else 0; dS = scale P (dP - Dlt).  Thread t takes row t/4 of
+// the tile, 16 columns; dS goes out row-major, P and dS also into LDS and out
+// transposed (P^T, dS^T: row = key, column = query).
+__global__ void __launch_bounds__(256)
+bwd512_ds_kernel(const float* __restrict__ Sm, const float* __restrict__ dPm,
+                 const float* __restrict__ LSE, const float* __restrict__ dlt,
+                 _Float16* __restrict__ dS, _Float16* __restrict__ PT, _Float16* __restrict__ dST,
+                 int S, int Sp, int T, int causal, float scale)
+{
+    constexpr int LD = 64 + 8;  // padded LDS row (halfs)
+    __shared__ _Float16 tp[64 * LD];
+    __shared__ _Float16 td[64 * LD];
+    const int tiles = T * T;
+    const int bh = blockIdx.x / tiles, rem = blockIdx.x % tiles;
+    const int bi = rem / T, bj = rem % T;
+    const int tid = threadIdx.x;
+    const int r = tid >> 2, c0 = 16 * (tid & 3);
+    const int i = bi * 64 + r;
+    const bool live = (!causal || bj <= bi) && i < S;
+    float lse = 0.f, dl = 0.f;
+    if (live) {
+        lse = LSE[(size_t)bh * S + i];
+        dl = dlt[(size_t)bh * S + i];
+    }
+    float sv[16], dpv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sv[e] = dpv[e] = 0.f;
+    if (live) {
+        const float4* s4 = reinterpret_cast<const float4*>(Sm + ((size_t)bh * S + i) * Sp + bj * 64 + c0);
+        const float4* d4 = reinterpret_cast<const float4*>(dPm + ((size_t)bh * S + i) * Sp + bj * 64 + c0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 a = s4[q], b = d4[q];
+            sv[4 * q] = a.x, sv[4 * q + 1] = a.y, sv[4 * q + 2] = a.z, sv[4 * q + 3] = a.w;
+            dpv[4 * q] = b.x, dpv[4 * q + 1] = b.y, dpv[4 * q + 2] = b.z, dpv[4 * q + 3] = b.w;
+        }
+    }
+    uint32_t dsw[8];
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+        _Float16 ph[2], dh[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int j = bj * 64 + c0 + e + u;
+            const bool vis = live && j < S && (!causal || j <= i);
+            // a masked entry may hold garbage (never written): select, not multiply
+            const float p = vis ? __builtin_amdgcn_exp2f((sv[e + u] - lse) * kLog2e) : 0.f;
+            const float ds = vis ? scale * p * (dpv[e + u] - dl) : 0.f;
+            ph[u] = (_Float16)p;
+            dh[u] = (_Float16)ds;
+            tp[r * LD + c0 + e + u] = ph[u];
+            td[r * LD + c0 + e + u] = dh[u];
+        }
+        dsw[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, dh[0]) |
+                     ((uint32_t)__builtin_bit_cast(uint16_t, dh[1]) << 16);
+    }
+    if (i < S) {
+        u32x4* dst = reinterpret_cast<u32x4*>(dS + ((size_t)bh * S + i) * Sp + bj * 64 + c0);
+        dst[0] = u32x4{dsw[0], dsw[1], dsw[2], dsw[3]};
+        dst[1] = u32x4{dsw[4], dsw[5], dsw[6], dsw[7]};
+    }
+    __syncthreads();
+    // transposed: row r of the output tile is key j = bj*64 + r, columns are
+    // the queries bi*64 + c0 .. +15
+    const int j = bj * 64 + r;
+    if (j < S) {
+        uint32_t pw[8], tw[8];
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+            pw[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, tp[(c0 + e) * LD + r]) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, tp[(c0 + e + 1) * LD + r]) << 16);
+            tw[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, td[(c0 + e) * LD + r]) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, td[(c0 + e + 1) * LD + r]) << 16);
+        }
+        u32x4* pd = reinterpret_cast<u32x4*>(PT + ((size_t)bh * S + j) * Sp + bi * 64 + c0);
+        u32x4* dd = reinterpret_cast<u32x4*>(dST + ((size_t)bh * S + j) * Sp + bi * 64 + c0);
+        pd[0] = u32x4{pw[0], pw[1], pw[2], pw[3]};
+        pd[1] = u32x4{pw[4], pw[5], pw[6], pw[7]};
+        dd[0] = u32x4{tw[0], tw[1], tw[2], tw[3]};
+        dd[1] = u32x4{tw[4], tw[5], tw[6], tw[7]};
+    }
+}
+
 }  // namespace
 
 int unfused_row_stride(int S) { return (S + 63) / 64 * 64; }
@@ -373,6 +492,53 @@ hipError_t launch_unfused(const FwdArgs& a, void* workspace) {
     if (a.D == 64) return launch_pv<64>(a, P, Sp);
     if (a.D == 128) return launch_pv<128>(a, P, Sp);
     return launch_pv<512>(a, P, Sp);
+}
+
+}  // namespace attn
+
+namespace attn {
+
+size_t bwd512_workspace_bytes(int B, int H, int S) {
+    const size_t bh = (size_t)B * H, n = (size_t)S * unfused_row_stride(S);
+    // S, dP (fp32); dS, P^T, dS^T (fp16); Dlt (fp32 per row)
+    return bh * n * (4 + 4 + 2 + 2 + 2) + bh * S * 4;
+}
+
+hipError_t launch_bwd512(const BwdArgs& a) {
+    const int S = a.S, Sp = unfused_row_stride(S), BH = a.B * a.H;
+    const size_t n = (size_t)BH * S * Sp;
+    float* Sm = reinterpret_cast<float*>(a.workspace);
+    float* dPm = Sm + n;
+    _Float16* dS = reinterpret_cast<_Float16*>(dPm + n);
+    _Float16* PT = dS + n;
+    _Float16* dST = PT + n;
+    float* dlt = reinterpret_cast<float*>(dST + n);
+    const hipStream_t st = (hipStream_t)a.stream;
+    const _Float16* q = (const _Float16*)a.q;
+    const _Float16* k = (const _Float16*)a.k;
+    const _Float16* v = (const _Float16*)a.v;
+    const _Float16* dO = (const _Float16*)a.dout;
+    const int TQ = (S + 63) / 64;
+    const dim3 qk_grid((unsigned)(BH * TQ * ((TQ + kQkChunk - 1) / kQkChunk)));
+    hipLaunchKernelGGL((qk_kernel<256, false>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 512, 0, a.causal, a.scale);
+    hipLaunchKernelGGL((qk_kernel<256, true>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 512, 256, a.causal, a.scale);
+    hipLaunchKernelGGL((qk_kernel<256, false>), qk_grid, dim3(256), 0, st, dO, v, dPm, BH, S, Sp, 512, 0, a.causal, 1.0f);
+    hipLaunchKernelGGL((qk_kernel<256, true>), qk_grid, dim3(256), 0, st, dO, v, dPm, BH, S, Sp, 512, 256, a.causal, 1.0f);
+    const int BHS = BH * S;
+    hipLaunchKernelGGL(bwd512_delta_kernel, dim3((unsigned)((BHS + 3) / 4)), dim3(256), 0, st, dO,
+                       (const _Float16*)a.o, dlt, BHS);
+    hipLaunchKernelGGL(bwd512_ds_kernel, dim3((unsigned)(BH * TQ * TQ)), dim3(256), 0, st, Sm, dPm,
+                       a.lse, dlt, dS, PT, dST, S, Sp, TQ, a.causal, a.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // dV = P^T dO, dK = dS^T Q (rows = keys, every column), dQ = dS K (causal rows)
+    using G = PvGeo<512>;
+    const dim3 pv_grid((unsigned)(BH * ((S + G::BM - 1) / G::BM)));
+    hipLaunchKernelGGL(pv_kernel<512>, pv_grid, dim3(256), 0, st, PT, dO, (_Float16*)a.dv, S, Sp, 0);
+    hipLaunchKernelGGL(pv_kernel<512>, pv_grid, dim3(256), 0, st, dST, q, (_Float16*)a.dk, S, Sp, 0);
+    hipLaunchKernelGGL(pv_kernel<512>, pv_grid, dim3(256), 0, st, dS, k, (_Float16*)a.dq, S, Sp,
+                       (int)a.causal);
+    return hipGetLastError();
 }
 
 }  // namespace attn

@@ -198,6 +198,13 @@ def test_decode_validation(L):
 def test_bwd_workspace_bytes(L):
     assert L.attn_bwd_workspace_bytes(2, 3, 1000) == 2 * 3 * 1000 * 4
     assert L.attn_bwd_workspace_bytes(0, 3, 1000) == 0
+    for D in (64, 128):
+        assert L.attn_bwd_workspace_bytes_d(2, 3, 1000, D) == 2 * 3 * 1000 * 4
+    # D = 512: S, dP (fp32), dS, P^T, dS^T (fp16) of S x Sp, Sp = S rounded up
+    # to 64, plus one float per row
+    sp = 1024
+    assert L.attn_bwd_workspace_bytes_d(2, 3, 1000, 512) == 6 * (1000 * sp * 14 + 1000 * 4)
+    assert L.attn_bwd_workspace_bytes_d(0, 3, 1000, 512) == 0
 
 
 def test_bwd_validation(L):
@@ -217,7 +224,8 @@ def test_bwd_validation(L):
     assert bwd(do=None) == C["ATTN_ERR_NULL"]
     assert bwd(dv=None) == C["ATTN_ERR_NULL"]
     assert bwd(S=0) == C["ATTN_ERR_SHAPE"]
-    assert bwd(D=512) == C["ATTN_ERR_HEAD_DIM"]
+    # D = 512 needs its larger workspace
+    assert bwd(D=512) == C["ATTN_ERR_WORKSPACE"]
     assert bwd(D=96) == C["ATTN_ERR_HEAD_DIM"]
     assert bwd(scale=math.inf) == C["ATTN_ERR_SCALE"]
     assert bwd(ws=None) == C["ATTN_ERR_WORKSPACE"]

@@ -64,7 +64,10 @@ def problem(seed, B, H, S, D, sigma=1.0):
     (1, 2, 200, 64, True), (1, 2, 200, 128, True), (2, 2, 129, 128, False),
     (1, 3, 64, 64, False), (1, 1, 1, 128, True), (1, 1, 1, 64, False),
     (1, 2, 257, 64, False), (1, 1, 33, 128, True), (2, 1, 320, 128, True),
-    (1, 2, 65, 64, True)])
+    (1, 2, 65, 64, True),
+    # D = 512: the materialised form (S, dP, dS, P^T, dS^T in the workspace)
+    (1, 2, 200, 512, True), (1, 1, 129, 512, False), (2, 1, 64, 512, True),
+    (1, 1, 1, 512, True), (1, 1, 33, 512, False)])
 def test_bwd_small(gpu, oracle_mod, B, H, S, D, causal):
     seed = 70_000 + 97 * S + D + int(causal)
     q, k, v, do = problem(seed, B, H, S, D)
@@ -83,14 +86,12 @@ def test_bwd_small(gpu, oracle_mod, B, H, S, D, causal):
     check_grads(got, ref, f"S={S} D={D} causal={causal}", zero_bound)
 
 
-@pytest.mark.parametrize("c", [1, 2, 3, 4])
+@pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
 def test_bwd_workload_shapes(gpu, oracle_mod, c):
     """The forward workloads' shapes and inputs, with dO drawn like Q; the GPU
     runs the full problem and the oracle checks a sample of (batch, head)
     pairs (heads are independent, so slicing the inputs is exact)."""
     w = inputs.WORKLOADS[c]
-    if w.D not in (64, 128):
-        pytest.skip("the backward covers D = 64 and 128")
     q, k, v = w.qkv()
     do = rnd(w.seed_base + 50, q.shape)
     log(f"bwd workload {w.name}")
@@ -134,9 +135,24 @@ def test_bwd_dk_sums_to_zero(gpu):
     assert np.all(tot <= 5e-3 * mag)
 
 
-def test_bwd_repeat_is_bit_identical(gpu):
-    q, k, v, do = problem(72_000, 2, 3, 300, 64)
+@pytest.mark.parametrize("D", [64, 512])
+def test_bwd_repeat_is_bit_identical(gpu, D):
+    q, k, v, do = problem(72_000, 2, 3, 300, D)
     a = run_bwd(gpu, q, k, v, do, True, 0.125)
     b = run_bwd(gpu, q, k, v, do, True, 0.125)
     for x, y in zip(a, b):
         assert np.array_equal(x.view(np.uint16), y.view(np.uint16))
+
+
+def test_bwd_d512_dk_sums_to_zero(gpu):
+    """The zero-sum property of the key gradients at workload 5's shape
+    (B=1 H=8 S=1024 D=512 causal) in full."""
+    w = inputs.WORKLOADS[5]
+    q, k, v = w.qkv()
+    do = rnd(w.seed_base + 50, q.shape)
+    _, dk, _ = run_bwd(gpu, q, k, v, do, w.causal, w.scale)
+    dk = dk.astype(np.float64)
+    tot = np.abs(dk.sum(axis=2))
+    mag = np.abs(dk).sum(axis=2)
+    log(f"D=512 sum_j dK_j: relative to sum|dK| {float((tot / mag).max()):.3g}")
+    assert np.all(tot <= 5e-3 * mag)
