@@ -13,18 +13,19 @@
 //   * A workgroup (4 waves) owns 64 query rows.  Wave w handles row group
 //     rg = w & 1 (32 rows) and head-dim half dh = w >> 1 (256 dims).
 //   * Per 32-key tile, wave (rg, dh) computes the partial S^T over its 256
-//     dims (16 v_mfma_f32_32x32x16_f16), publishes it in LDS, and adds its
-//     partner's (rg, 1-dh) partial: both waves then hold the same
-//     S = S_0 + S_1 (fp32 addition is commutative, so they agree bit for bit)
-//     and run the same online softmax.
-//   * Each wave then accumulates O^T for its own 256 output dims
-//     (16 MFMAs), reading V^T with ds_read_b64_tr_b16, like the smaller-D
-//     kernel.  Splitting P V along the output dims is what the notes call the
+//     dims (16 v_mfma_f32_32x32x16_f16), publishes it in LDS, and after the
+//     next barrier adds its partner's (rg, 1-dh) partial: both waves then
+//     hold the same S = S_0 + S_1 (fp32 addition is commutative, so they
+//     agree bit for bit) and run the same online softmax.
+//   * Each wave accumulates O^T for its own 256 output dims (16 MFMAs),
+//     reading V^T with ds_read_b64_tr_b16, like the smaller-D kernel.
+//     Splitting P V along the output dims is what the notes call the
 //     pv_n_tile knob; it keeps a wave's output accumulator at 128 registers.
-//   * K (padded rows) and V (XOR-swizzled rows) stream through two LDS stages,
-//     loaded straight from global memory into LDS (bounds-checked buffer loads
-//     with the LDS destination bit, one 1 KB row per instruction, no staging
-//     registers).
+//   * K and V rows (XOR-swizzled in 16-byte chunks) stream through two LDS
+//     stages each, loaded straight from global memory into LDS
+//     (bounds-checked buffer loads with the LDS destination bit, one 1 KB row
+//     per instruction, no staging registers), issued between the matrix
+//     instructions of a two-phase software pipeline (run(), below).
 //
 // Split-KV.  Eight heads of 1024 rows give only 128 workgroups for 256 CUs, and
 // under causal masking the last query tile does 32 key tiles while the first
