@@ -33,7 +33,12 @@
  *   - Any S >= 1 is accepted (up to the size limit below): ragged tails are
  *     masked, never read out of bounds.
  *   - Deterministic: the same inputs give the same output bytes (no atomics,
- *     fixed reduction order).
+ *     fixed reduction order).  The kernel depends on the whole call: at
+ *     D = 128 a call with B*H*ceil(S/128) >= 512 query tiles of 128 rows
+ *     runs the 128-row kernel, a smaller one the 64-row kernel, so a (b, h)
+ *     slice of a large call launched on its own agrees with its slice of the
+ *     call to rounding (both within the parity gate), bit for bit only when
+ *     both calls take the same kernel.
  *
  * Ownership and synchronisation
  *   The caller allocates and owns every buffer; the library never allocates

@@ -140,3 +140,27 @@ def test_rows_head_dim_coverage(gpu, oracle_mod):
         sc = 2 / math.sqrt(D)
         o, lse = run(gpu, q, k, v, True, sc)
         sample_check(oracle_mod, q, k, v, o, lse, True, sc, f"coverage half={half}")
+
+
+def test_rows_slice_alone_matches_within_gate(gpu, oracle_mod):
+    """P11 across the dispatch threshold: a (b, h) slice of a call routed to
+    the 128-row kernel, launched alone, runs the 64-row kernel; the two agree
+    to rounding (each within the gate of the oracle) and, for a slice of a
+    call that is itself routed, bit for bit."""
+    B, H, S = 1, 256, 200
+    assert routed(B, H, S) and not routed(1, 1, S)
+    q, k, v = (rnd(35_000 + t, (B, H, S, D)) for t in range(3))
+    sc = 1 / math.sqrt(D)
+    o, lse = run(gpu, q, k, v, True, sc)
+    h = 77
+    o1, l1 = run(gpu, q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], True, sc)
+    o_ref, l_ref = oracle_mod.attn_fwd(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], True, sc)
+    check(o[:, h:h + 1], lse[:, h:h + 1], o_ref, l_ref, "slice of the routed call")
+    check(o1, l1, o_ref, l_ref, "slice alone")
+    # the same slice inside another routed call (different neighbours) is bit-exact
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    for t in (q2, k2, v2):
+        t[:, :h] = rnd(35_100, t[:, :h].shape)
+    o2, l2 = run(gpu, q2, k2, v2, True, sc)
+    assert np.array_equal(o[:, h:h + 1], o2[:, h:h + 1])
+    assert np.array_equal(lse[:, h:h + 1], l2[:, h:h + 1])
