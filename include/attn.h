@@ -119,7 +119,7 @@ int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o,
  * workspace and results as attn_fwd_decode; its chunks are 64-key tiles).
  * D = 512: the key range of every 64-row query tile is cut into
  * chunks of at most C = ceil(ceil(S/32) / splits) 32-key tiles; each chunk is
- * one workgroup that leaves its partial state (unnormalised O in fp32, row
+ * one workgroup that leaves its partial state (its own normalised O in fp16, row
  * max and row sum) in `workspace`, and a second kernel merges the chunks of
  * each row in chunk order (deterministic).  The merge over DISJOINT key sets
  * is exact up to rounding (STAGE_D.md notes, section "2. External k_sub Merge

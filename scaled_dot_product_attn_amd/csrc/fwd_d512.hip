@@ -31,7 +31,7 @@
 // under causal masking the last query tile does 32 key tiles while the first
 // does 2.  The split variant cuts every query tile's key range into chunks of
 // at most C 32-key tiles; each chunk is one workgroup that leaves its partial
-// state (unnormalised O in fp32, row max m and row sum l) in a workspace, and
+// state (its own normalised O in fp16, row max m and row sum l) in a workspace, and
 // a second kernel merges the chunks of a row in chunk order.  The merge is
 // exact because the chunks hold DISJOINT key sets (STAGE_D.md notes, section
 // "2. External k_sub Merge is Mathematically Impossible": outputs over
@@ -76,6 +76,12 @@ __device__ __forceinline__ int swz_k512(int r) { return r & 15; }
 // V row swizzle: XOR chunk bits 2-3 with the row's low two bits, so that the
 // four rows of a transposed read hit different banks.
 __device__ __forceinline__ int swz_v512(int r) { return 4 * (r & 3); }
+
+// A chunk's slot: its normalised partial output O_c / l_c as fp16
+// [64][512] (kSlotOFloats floats' worth of bytes), then m [64] (log2 units)
+// and l [64] in fp32.
+constexpr size_t kSlotOFloats = (size_t)G512::BM * G512::D / 2;
+constexpr size_t kSlotFloats = kSlotOFloats + 2 * G512::BM;
 
 struct Fwd512 {
     using G = G512;
@@ -357,7 +363,7 @@ struct Fwd512 {
 
     // Query tile qt over key tiles [kt0, kt1).  part == nullptr: write O and
     // LSE; otherwise leave the partial state in the chunk's workspace slot:
-    // unnormalised O as fp32 [64][512], then m[64] (log2 units) and l[64].
+    // O / l as fp16 [64][512], then m[64] (log2 units) and l[64] in fp32.
     //
     // Software pipeline, per key tile i, in two phases with a barrier each:
     //   P: wait for V(i-1) (K(i+1) may still be in flight), barrier;
@@ -406,10 +412,15 @@ struct Fwd512 {
         // the last one, for the upper row group of a causal tile) go through
         // the same steps: every key masked, P = 0, nothing changes.
 
-        // prologue: K(kt0), K(kt0+1); the partial S(kt0)
+        // prologue: K(kt0), K(kt0+1); the partial S(kt0) as soon as Q and
+        // K(kt0) are in (K(kt0+1) is waited for at the next barrier)
         dma(K, ks(0), kt0, true);
-        if (nt > 1) dma(K, ks(1), kt0 + 1, true);
-        barrier_dma();
+        if (nt > 1) {
+            dma(K, ks(1), kt0 + 1, true);
+            barrier_dma_but8();
+        } else {
+            barrier_dma();
+        }
         floatx16 s_cur = qk_half<false>(qf, 0);
         publish(xch(), s_cur);
 
@@ -453,16 +464,26 @@ struct Fwd512 {
         // writes its 256 output dims.
         const float lt = sum_halves(l);
         if (part) {
-            float* po = part + (size_t)(32 * rg + n) * G::D + G::DH * dh;
+            // the chunk's own normalised output O / l in fp16 (|O / l| <=
+            // max |V|; 0 where the chunk saw no key of the row), then m, l
+            const float pinv = lt > 0.f ? 1.0f / lt : 0.f;
+            _Float16* po = reinterpret_cast<_Float16*>(part) + (size_t)(32 * rg + n) * G::D +
+                           G::DH * dh;
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    *reinterpret_cast<float4*>(po + 32 * b + 8 * q4 + 4 * g) =
-                        float4{o[b][4 * q4], o[b][4 * q4 + 1], o[b][4 * q4 + 2], o[b][4 * q4 + 3]};
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    u32x2 pk;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        pk[h] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(o[b][4 * q4 + 2 * h] * pinv)) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(o[b][4 * q4 + 2 * h + 1] * pinv)) << 16);
+                    *reinterpret_cast<u32x2*>(po + 32 * b + 8 * q4 + 4 * g) = pk;
+                }
+            float* pml = part + kSlotOFloats;
             if (dh == 0 && g == 0) {
-                part[G::BM * G::D + 32 * rg + n] = m;
-                part[G::BM * G::D + G::BM + 32 * rg + n] = lt;
+                pml[32 * rg + n] = m;
+                pml[G::BM + 32 * rg + n] = lt;
             }
             return;
         }
@@ -520,7 +541,7 @@ struct Chunking {
     }
 };
 
-constexpr size_t kSlotFloats = (size_t)G512::BM * G512::D + 2 * G512::BM;
+
 
 __global__ void __launch_bounds__(256, 1)
 fwd512_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
@@ -584,22 +605,29 @@ merge512_kernel(const float* __restrict__ ws, _Float16* __restrict__ O, float* _
     const int d0 = 16 * (threadIdx.x & 31);
     const int row = qt * G::BM + r;
     float mt = kNegInf;
-    for (int cc = 0; cc < nch; ++cc) mt = fmaxf(mt, slot0[cc * kSlotFloats + G::BM * G::D + r]);
+    for (int cc = 0; cc < nch; ++cc) mt = fmaxf(mt, slot0[cc * kSlotFloats + kSlotOFloats + r]);
+    // O = sum_c w_c l_c (O_c / l_c) / sum_c w_c l_c with w_c = 2^(m_c - m*);
+    // a chunk that saw no key of this row has l = 0 (and a zero O_c / l_c)
     float lsum = 0.f;
     float4 acc[4] = {};
     for (int cc = 0; cc < nch; ++cc) {
         const float* sl = slot0 + cc * kSlotFloats;
-        // a chunk that saw no key of this row has l = 0 and zero O
-        const float wgt = __builtin_amdgcn_exp2f(sl[G::BM * G::D + r] - mt);
-        lsum += wgt * sl[G::BM * G::D + G::BM + r];
-        const float4* x = reinterpret_cast<const float4*>(sl + (size_t)r * G::D + d0);
+        const float wl = __builtin_amdgcn_exp2f(sl[kSlotOFloats + r] - mt) *
+                         sl[kSlotOFloats + G::BM + r];
+        lsum += wl;
+        const u32x4* x = reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const _Float16*>(sl) + (size_t)r * G::D + d0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float4 y = x[e];
-            acc[e].x += wgt * y.x;
-            acc[e].y += wgt * y.y;
-            acc[e].z += wgt * y.z;
-            acc[e].w += wgt * y.w;
+        for (int e2 = 0; e2 < 2; ++e2) {
+            const half8 y = __builtin_bit_cast(half8, x[e2]);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                float4& a = acc[2 * e2 + e];
+                a.x += wl * (float)y[4 * e];
+                a.y += wl * (float)y[4 * e + 1];
+                a.z += wl * (float)y[4 * e + 2];
+                a.w += wl * (float)y[4 * e + 3];
+            }
         }
     }
     if (row >= S) return;

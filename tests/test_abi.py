@@ -120,7 +120,7 @@ def splitkv_units(S, causal, splits):
                                              (300, 1, 3), (65, 0, 16), (1, 1, 8)])
 def test_splitkv_workspace_bytes(L, S, causal, splits):
     units, T = splitkv_units(S, causal, splits)
-    slot = (64 * 512 + 2 * 64) * 4
+    slot = 64 * 512 * 2 + 2 * 64 * 4   # fp16 O_c / l_c, then m and l in fp32
     expect = 0 if units == T else 2 * 3 * units * slot
     assert L.attn_fwd_splitkv_workspace_bytes(2, 3, S, 512, causal, splits) == expect
     if (S, causal, splits) == (1024, 1, 4):
@@ -282,7 +282,7 @@ def test_unit_counts_do_not_wrap(L):
     S, splits = (1 << 22) - 64, 1 << 20      # D = 512: just under a 4 GiB slice
     units, T = splitkv_units(S, 1, splits)
     assert units > 2**31
-    slot = (64 * 512 + 2 * 64) * 4
+    slot = 64 * 512 * 2 + 2 * 64 * 4
     assert L.attn_fwd_splitkv_workspace_bytes(1, 1, S, 512, 1, splits) == units * slot
     big = 0x1_0000_0000_0000
     q, k, v, o, lse = (big * (i + 1) for i in range(5))
