@@ -27,6 +27,13 @@
 // the LDS destination bit, no staging registers) through two K and two V
 // slots; the Q tile comes in the same way and stays in registers.
 //
+// Causal balance.  When the pairs alone still give two workgroups per CU, a
+// workgroup runs two query tiles of one (batch, head), T-1-u and then u, so
+// every workgroup carries T+1 tile-lengths of keys; the second tile's prologue
+// loads go out right after the first tile's last barrier, ahead of its
+// epilogue, and its K/V chunks are a prefix of those the first tile just read
+// (same XCD L2).  Otherwise one tile per workgroup, heaviest tiles first.
+//
 // Causal masking.  Wave w's rows see every key of the chunks before its
 // diagonal chunk cw = (q0 + 32w) / 32, part of chunk cw, and none after it.
 // So the pipelined iterations never mask; chunk cw is the wave's last,
@@ -223,8 +230,25 @@ struct Rows {
         s_cur = s_next;
     }
 
+    // The prologue loads of query tile qt: K(0), the Q tile, V(0) and, when
+    // the tile has more than one chunk, K(1), in that order (2 + 8 + 2 + 2
+    // loads of this wave).
+    __device__ __forceinline__ void prologue_loads(int qt, int nk) const {
+        dma(sl.k[0], 0, true);
+        const auto rq = rows_rsrc(Q, qt * G::BM, G::BM);
+#pragma unroll
+        for (int u = 0; u < G::QPIECES; ++u) dma_piece(sl.q, rq, w * G::QPIECES + u, true);
+        dma(sl.v[0], 0, false);
+        if (nk > 1) dma(sl.k[1], 1, true);
+    }
+    static_assert(G::PIECES == 2, "the prologue waits count 2 loads per chunk");
+
     // Query tile qt (rows 128 qt ..), chunks 0 .. nk-1 of the workgroup.
-    __device__ void run(int qt, int nk) {
+    // issued: the prologue loads were issued already (by the previous tile of
+    // this workgroup, after its last barrier).  nxt >= 0: after this tile's
+    // last barrier, when no wave reads the LDS any more, issue the prologue
+    // loads of tile nxt (nk_nxt chunks) ahead of this tile's epilogue.
+    __device__ void run(int qt, int nk, bool issued, int nxt, int nk_nxt) {
         const int q0 = qt * G::BM;
         const int row = q0 + 32 * w + n;
         // last key this lane's row may see
@@ -233,19 +257,25 @@ struct Rows {
         // last key); every key of the earlier ones is visible to all its rows
         const int cw = CAUSAL ? min(q0 + 32 * w, S - 1) / G::BN : nk - 1;
 
-        // prologue: K(0), Q, V(0), K(1) into their slots; wait for all of
-        // them; the Q fragments (sign-flipped for a negative scale), S(0),
-        // the K(1) and V(0) fragments; a barrier (every wave is done with
-        // K(0)); then the loads of K(2) and V(1)
-        dma(sl.k[0], 0, true);
-        {
-            const auto rq = rows_rsrc(Q, q0, G::BM);
-#pragma unroll
-            for (int u = 0; u < G::QPIECES; ++u) dma_piece(sl.q, rq, w * G::QPIECES + u, true);
+        // prologue: K(0), Q, V(0), K(1) into their slots; wait for K(0) and
+        // Q, barrier; the Q fragments (sign-flipped for a negative scale) and
+        // S(0); wait for V(0) and K(1), barrier; the K(1) and V(0)
+        // fragments; a barrier (every wave is done with K(0)); then the loads
+        // of K(2) and V(1).  Loads complete in order, so leaving the last
+        // 2 or 4 outstanding waits for K(0) and Q; after loads issued by the
+        // previous tile, its O stores came later, and the first wait takes
+        // everything.
+        if (!issued) {
+            prologue_loads(qt, nk);
+            if (nk > 1)
+                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
-        dma(sl.v[0], 0, false);
-        if (nk > 1) dma(sl.k[1], 1, true);
-        barrier_dma();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
         half8 qf[D / 16];
         {
             const int qrow = 32 * w + n;
@@ -263,6 +293,7 @@ struct Rows {
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) kf[kk] = read_k1(sl.k[0], kk);
         floatx16 s_cur = qk(kf, qf);
+        barrier_dma();
         if (nk > 1) {
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) kf[kk] = read_k1(sl.k[1], kk);
@@ -319,7 +350,8 @@ struct Rows {
             else
                 loads_only<0>(j, nk);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // every load of this tile was waited for before the last barrier
+        if (nxt >= 0) prologue_loads(nxt, nk_nxt);
 
         // O = O / l, fp16, and LSE.  Register r of block b holds head dim
         // 32b + 8(r/4) + 4g + r%4; lanes n and n+32 swap halves
@@ -354,7 +386,7 @@ struct Rows {
     }
 };
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool PAIRED>
 __global__ void __launch_bounds__(256, 2)
 fwd_rows_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                 const _Float16* __restrict__ V, _Float16* __restrict__ O, float* __restrict__ LSE,
@@ -370,10 +402,11 @@ fwd_rows_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     const int bh = blockIdx.x % BH;
     const int u = blockIdx.x / BH;
     // causal: the heaviest query tiles first, so that the dispatcher, handing
-    // out workgroups in order as CU slots free up, fills in the light ones last
-    const int qt = CAUSAL ? T - 1 - u : u;
-    const int kv_end = CAUSAL ? min(S, (qt + 1) * G::BM) : S;
-    const int nk = (kv_end + G::BN - 1) / G::BN;
+    // out workgroups in order as CU slots free up, fills in the light ones
+    // last.  Paired (causal, many tiles): workgroup u runs tile T-1-u and then
+    // tile u of its (batch, head), T+1 tile-lengths of work for every
+    // workgroup.
+    const int qt0 = CAUSAL ? T - 1 - u : u;
 
     Rows<CAUSAL> f;
     f.Q = Q;
@@ -395,7 +428,17 @@ fwd_rows_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     f.g = f.lane >> 5;
     f.n = f.lane & 31;
     f.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    f.run(qt, nk);
+    const int nk0 = ((CAUSAL ? min(S, (qt0 + 1) * G::BM) : S) + G::BN - 1) / G::BN;
+    if (PAIRED && u != qt0) {
+        const int nk1 = (min(S, (u + 1) * G::BM) + G::BN - 1) / G::BN;
+        f.run(qt0, nk0, false, u, nk1);
+        // opaque lane indices: the second tile recomputes its per-lane
+        // offsets instead of keeping the first tile's alive across it
+        asm volatile("" : "+v"(f.lane), "+v"(f.g), "+v"(f.n));
+        f.run(u, nk1, true, -1, 0);
+    } else {
+        f.run(qt0, nk0, false, -1, 0);
+    }
 }
 
 }  // namespace
@@ -406,15 +449,22 @@ hipError_t launch_fused_rows_d128(const FwdArgs& a) {
     const int T = (a.S + G::BM - 1) / G::BM;
     const float c = fabsf(a.scale) * 1.44269504088896340736f;
     const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
-    const dim3 grid((unsigned)((long long)BH * T));
-    if (a.causal)
-        hipLaunchKernelGGL((fwd_rows_kernel<true>), grid, dim3(G::NT), 0, (hipStream_t)a.stream,
-                           (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,
-                           (_Float16*)a.o, a.lse, BH, a.S, c, qsign);
+    // causal tiles in pairs (T-1-u, u) when the pairs alone still give two
+    // workgroups per CU (256 CUs)
+    const int pairs = (T + 1) / 2;
+    const int paired = a.causal && (long long)BH * pairs >= 512;
+    const dim3 grid((unsigned)((long long)BH * (paired ? pairs : T)));
+#define ROWS_LAUNCH(C, P)                                                                   \
+    hipLaunchKernelGGL((fwd_rows_kernel<C, P>), grid, dim3(G::NT), 0, (hipStream_t)a.stream, \
+                       (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,     \
+                       (_Float16*)a.o, a.lse, BH, a.S, c, qsign)
+    if (paired)
+        ROWS_LAUNCH(true, true);
+    else if (a.causal)
+        ROWS_LAUNCH(true, false);
     else
-        hipLaunchKernelGGL((fwd_rows_kernel<false>), grid, dim3(G::NT), 0, (hipStream_t)a.stream,
-                           (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,
-                           (_Float16*)a.o, a.lse, BH, a.S, c, qsign);
+        ROWS_LAUNCH(false, false);
+#undef ROWS_LAUNCH
     return hipGetLastError();
 }
 
