@@ -128,13 +128,16 @@ __device__ __forceinline__ void softmax_block(floatx16 s, int lim, float c, floa
     // weights against reference mref: P^T in fp16 into pf, and this lane's
     // sum in fp32 (four partial sums, then a tree)
     auto weights = [&](float mref) {
-        float q[4] = {0.f, 0.f, 0.f, 0.f};
+        float q[4];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float t = __builtin_fmaf(s[r], c, -mref);
             if (MASK && (8 * (r >> 2) + (r & 3)) > lim) t = kNegInf;
             const float e = __builtin_amdgcn_exp2f(t);
-            q[r & 3] += e;
+            if (r < 4)
+                q[r] = e;
+            else
+                q[r & 3] += e;
             pf[r >> 3][r & 7] = (_Float16)e;
         }
         return (q[0] + q[1]) + (q[2] + q[3]);

@@ -203,7 +203,9 @@ struct Rows {
     //   V(j), both last read before this barrier), every one by one K(j+2)
     //   fragment read and the read of the V(j+1) fragment into the registers
     //   it consumed.
-    template <int P>
+    // ALL: the caller knows j + 3 < nk (both loads and the K read happen; no
+    // branches around them).
+    template <int P, bool ALL>
     __device__ __forceinline__ void iter(int j, int nk, int lim0, const half8* qf, half8* kf,
                                          half8 (*vf)[NB], floatx16& s_cur, float& m, float& l,
                                          floatx16* o) {
@@ -211,7 +213,7 @@ struct Rows {
         half8 pf[2];
         softmax_block<false, NB, true>(s_cur, lim0 - j * G::BN, c, m, l, o, pf);
         barrier_dma();
-        const bool dk = j + 3 < nk, dv = j + 2 < nk;
+        const bool dk = ALL || j + 3 < nk, dv = ALL || j + 2 < nk;
         const auto rk = rows_rsrc(K, (j + 3) * G::BN, G::BN);
         const auto rv = rows_rsrc(V, (j + 2) * G::BN, G::BN);
 #pragma unroll
@@ -248,6 +250,10 @@ struct Rows {
     // this workgroup, after its last barrier).  nxt >= 0: after this tile's
     // last barrier, when no wave reads the LDS any more, issue the prologue
     // loads of tile nxt (nk_nxt chunks) ahead of this tile's epilogue.
+    // STEADY: run the chunks whose loads all happen (j + 3 < nk) through a
+    // copy of the step without branches around its loads (faster with one
+    // workgroup per CU; with two, the branch-free copy measured slower).
+    template <bool STEADY>
     __device__ void run(int qt, int nk, bool issued, int nxt, int nk_nxt) {
         const int q0 = qt * G::BM;
         const int row = q0 + 32 * w + n;
@@ -316,12 +322,16 @@ struct Rows {
         const int lim0 = vis - 4 * g;  // minus 32 j for chunk j
         // the pipelined chunks before the diagonal (one barrier each)
         int j = 0;
+        for (; STEADY && j + 2 <= cw && j + 4 < nk; j += 2) {
+            iter<0, true>(j, nk, lim0, qf, kf, vf, s_cur, m, l, o);
+            iter<1, true>(j + 1, nk, lim0, qf, kf, vf, s_cur, m, l, o);
+        }
         for (; j + 2 <= cw; j += 2) {
-            iter<0>(j, nk, lim0, qf, kf, vf, s_cur, m, l, o);
-            iter<1>(j + 1, nk, lim0, qf, kf, vf, s_cur, m, l, o);
+            iter<0, false>(j, nk, lim0, qf, kf, vf, s_cur, m, l, o);
+            iter<1, false>(j + 1, nk, lim0, qf, kf, vf, s_cur, m, l, o);
         }
         if (j < cw) {
-            iter<0>(j, nk, lim0, qf, kf, vf, s_cur, m, l, o);
+            iter<0, false>(j, nk, lim0, qf, kf, vf, s_cur, m, l, o);
             ++j;
         }
         // the diagonal chunk j = cw: masked softmax, barrier, O += V^T P with
@@ -429,15 +439,18 @@ fwd_rows_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     f.n = f.lane & 31;
     f.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nk0 = ((CAUSAL ? min(S, (qt0 + 1) * G::BM) : S) + G::BN - 1) / G::BN;
-    if (PAIRED && u != qt0) {
-        const int nk1 = (min(S, (u + 1) * G::BM) + G::BN - 1) / G::BN;
-        f.run(qt0, nk0, false, u, nk1);
+    const bool two = PAIRED && u != qt0;
+    const int nk1 = (min(S, (u + 1) * G::BM) + G::BN - 1) / G::BN;
+    // one copy of the tile code for both tiles of a pair
+    int qt = qt0, nk = nk0;
+#pragma unroll 1
+    for (int it = 0; it < (two ? 2 : 1); ++it) {
         // opaque lane indices: the second tile recomputes its per-lane
         // offsets instead of keeping the first tile's alive across it
         asm volatile("" : "+v"(f.lane), "+v"(f.g), "+v"(f.n));
-        f.run(u, nk1, true, -1, 0);
-    } else {
-        f.run(qt0, nk0, false, -1, 0);
+        f.template run<!PAIRED>(qt, nk, it > 0, (it == 0 && two) ? u : -1, nk1);
+        qt = u;
+        nk = nk1;
     }
 }
 

@@ -56,6 +56,27 @@ def test_rows_ragged(gpu, oracle_mod, causal):
         sample_check(oracle_mod, q, k, v, o, lse, causal, sc, f"S={S} causal={causal}")
 
 
+def paired(B, H, S):
+    t = -(-S // 128)
+    return B * H * ((t + 1) // 2) >= 512
+
+
+@pytest.mark.parametrize("B,H,S", [(1, 512, 200), (2, 128, 300), (1, 128, 1000), (4, 64, 512)])
+def test_rows_paired_tiles(gpu, oracle_mod, B, H, S):
+    """Causal calls with at least 512 pairs of 128-row tiles, where one
+    workgroup runs tiles T-1-u and u of a head: even and odd tile counts (the
+    middle tile alone), ragged last tiles; every row of the sampled heads
+    against the oracle, and the call's bytes repeat."""
+    assert routed(B, H, S) and paired(B, H, S)
+    log(f"rows kernel paired B={B} H={H} S={S}")
+    q, k, v = (rnd(36_000 + 11 * S + t, (B, H, S, D)) for t in range(3))
+    sc = 1 / math.sqrt(D)
+    o, lse = run(gpu, q, k, v, True, sc)
+    sample_check(oracle_mod, q, k, v, o, lse, True, sc, f"paired B={B} H={H} S={S}", n_pick=3)
+    o2, lse2 = run(gpu, q, k, v, True, sc)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
 def test_rows_workload4_every_head(gpu, oracle_mod):
     """Workload 4 (B8 H32 S512) on the 128-row kernel, every one of the 256
     (batch, head) slices against the oracle."""
