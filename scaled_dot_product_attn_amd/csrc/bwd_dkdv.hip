@@ -9,29 +9,47 @@ using namespace detail;
 
 // dK and dV for one 64-key tile.  Wave (lo, hi): keys 32lo .. +31 of the tile,
 // query rows 32hi .. +31 of every query tile that sees the keys.
-//   S  = Q K^T  : A = Q rows (LDS), B = this wave's K rows (registers)
-//   dP = dO V^T : A = dO rows (LDS), B = this wave's V rows (registers)
+//   S  = Q K^T  : A = Q rows, B = this wave's K rows
+//   dP = dO V^T : A = dO rows, B = this wave's V rows
 //   dV^T += dO^T P, dK^T += Q^T dS : A = dO / Q columns (transposed LDS
 //                 reads), B = P / dS (score registers); the accumulators hold
 //                 lane = key, registers = head dims, so that rows are stored
 //                 from registers
+// Every operand comes from LDS (the K and V tiles stay there for the whole
+// walk, one stage holds the current Q and dO tiles), so that a wave holds
+// the two accumulators, the scores and a few fragments in flight: at most 256
+// registers, two workgroups per CU, and one workgroup's loads and barriers
+// run under the other's products.
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, 2)
 bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                 const _Float16* __restrict__ V, const _Float16* __restrict__ dO,
                 const float* __restrict__ dlt, const float* __restrict__ LSE,
                 _Float16* __restrict__ dK, _Float16* __restrict__ dV,
-                int BH, int S, float c, float scale, uint32_t qsign)
+                int BH, int S, float cs, float scale)
 {
     using G = GeoB<D>;
     constexpr int NB = G::NB;
-    // two stages of (Q tile, dO tile, LSE log2(e) [64], dlt[64])
-    constexpr int STAGE = 2 * G::TILE + 2 * 64 * 2;  // halfs
-    __shared__ __attribute__((aligned(1024))) _Float16 lds[2 * STAGE];
+    constexpr int PIECES = G::TILE * 2 / 1024 / G::NW;  // 1 KB pieces of a tile per wave
+    constexpr int RPP = 1024 / (2 * D);                 // rows per piece
+    // K tile, V tile, Q tile, dO tile, then LSE log2(e) [64] and Dlt [64]
+    __shared__ __attribute__((aligned(1024))) _Float16 lds[4 * G::TILE + 2 * 64 * 2];
+    static_assert(4 * (NB * 4) * 64 * 16 <= (4 * G::TILE + 2 * 64 * 2) * 2, "merge buffers fit");
+    using LdsPtr = __attribute__((address_space(3))) void*;
+    _Float16* const Ks = lds;
+    _Float16* const Vs = lds + G::TILE;
+    _Float16* const Qs = lds + 2 * G::TILE;
+    _Float16* const Os = lds + 3 * G::TILE;
+    float* const fl = reinterpret_cast<float*>(lds + 4 * G::TILE);
 
     const int T = (S + 63) / 64;
     const int bh = blockIdx.x % BH;
-    const int kt = blockIdx.x / BH;  // causal: kt = 0 sees the most query tiles, so runs first
+    // causal: the first half of the grid takes the key tiles that see the
+    // most query tiles (0, 1, ...), the second half the others (T-1, T-2,
+    // ...), so that workgroups i and i + grid/2, which share a CU when the
+    // grid fills the chip once, carry T+1 query tiles between them
+    const int j = blockIdx.x / BH;
+    const int kt = CAUSAL ? (j < (T + 1) / 2 ? j : T - 1 - (j - (T + 1) / 2)) : j;
     const int k0 = kt * 64;
 
     Bwd<D> f;
@@ -45,9 +63,53 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     f.hi = w >> 1;
     f.base = (size_t)bh * S * D;
     f.row_base = (size_t)bh * S;
-    f.c = c;
-    f.qsign = qsign;
     const int lo = f.lo, hi = f.hi, g = f.g, n = f.n, lane = f.lane;
+
+    // Piece u (< PIECES) of this wave's share of rows r0 .. r0+63 of t into
+    // the swizzled tile dst, straight from global memory into LDS; lane L of
+    // a 1 KB piece lands at byte 16 L of it, so it loads the logical chunk
+    // the swizzle puts there; rows past S read as zero.  M0 = the LDS
+    // address; the only waits on these loads are the explicit ones.
+    auto dma_tile = [&](_Float16* dst, const _Float16* t, int r0) {
+        const auto r = f.rsrc(t, r0);
+#pragma unroll
+        for (int u = 0; u < PIECES; ++u) {
+            const int piece = w * PIECES + u;
+            const int row = RPP * piece + lane / G::CPR;
+            const int logical = (lane % G::CPR) ^ swz_b<D>(row);
+            const uint32_t m0 = (uint32_t)(uintptr_t)(LdsPtr)(dst + piece * 512);
+            asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :
+                         : "v"((row * D + 8 * logical) * 2), "s"(r), "{m0}"(m0)
+                         : "memory");
+        }
+    };
+    // One row fragment: row r0 + n, head dims 16kk + 8g .. +7.
+    auto row1 = [&](const _Float16* tile, int r0, int kk) {
+        const int row = r0 + n;
+        return *reinterpret_cast<const half8*>(tile + row * D + 8 * ((2 * kk + g) ^ swz_b<D>(row)));
+    };
+    // One transposed fragment (head dims 32b + n of rows r0 + 16h +
+    // {4g .. 4g+3, 8+4g .. 8+4g+3}), as Bwd::cols.
+    auto col1 = [&](const _Float16* tile, int r0, int h, int b) {
+        const int n16 = n >> 4, jj = n & 15;
+        const int sub = (jj & 3) >> 1, half = jj & 1;
+        half4 part[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int row = r0 + 4 * g + (jj >> 2) + 16 * h + 8 * t;
+            const int chunk = (4 * b + 2 * n16 + sub) ^ swz_b<D>(row);
+            part[t] = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                                                    (lds_half4*)(tile + row * D + 8 * chunk + 4 * half)));
+        }
+        return half8{part[0][0], part[0][1], part[0][2], part[0][3],
+                     part[1][0], part[1][1], part[1][2], part[1][3]};
+    };
+    auto barrier_dma = [&]() {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
 
     floatx16 dk[NB], dv[NB];
 #pragma unroll
@@ -58,114 +120,69 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
             dv[b][r] = 0.f;
         }
 
+    // this workgroup's K and V tiles, resident for the whole walk
+    dma_tile(Ks, K, k0);
+    dma_tile(Vs, V, k0);
     const int qt0 = CAUSAL ? kt : 0;
-    u32x4 xq[G::CH], xo[G::CH];
-    float lv = 0.f, dv_ = 0.f;
-    auto stage_of = [&](int s) { return lds + s * STAGE; };
-    // The row values are loaded first and used only in put(): consumed
-    // right after the tile loads, they made the wave wait for those too.
-    auto fetch = [&](int qt) {
+    const int key = k0 + 32 * lo + n;
+    for (int qt = qt0; qt < T; ++qt) {
+        // every wave is done with the previous Q and dO tiles
+        barrier_dma();
+        dma_tile(Qs, Q, qt * 64);
+        dma_tile(Os, dO, qt * 64);
         if (f.tid < 64) {
-            const int row = qt * 64 + f.tid;
-            lv = row < S ? LSE[f.row_base + row] : 0.f;
-            dv_ = row < S ? dlt[f.row_base + row] : 0.f;
-        }
-        f.load(xq, Q, qt * 64);
-        f.load(xo, dO, qt * 64);
-    };
-    auto put = [&](int s) {
-        _Float16* st = stage_of(s);
-        f.store(st, xq);
-        f.store(st + G::TILE, xo);
-        if (f.tid < 64) {
-            float* fl = reinterpret_cast<float*>(st + 2 * G::TILE);
+            // rows past S: any finite value (their products are masked)
+            const int row = min(qt * 64 + f.tid, S - 1);
+            const float lv = LSE[f.row_base + row];
+            const float dv_ = dlt[f.row_base + row];
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             fl[f.tid] = lv * kLog2e;
             fl[64 + f.tid] = dv_;
         }
-    };
-    // All start-up loads are issued before the first wait: the first query
-    // tile, then this wave's K and V rows (B operands with k = head dim, kept
-    // for the whole walk).  A negative scale negates the logits through K.
-    fetch(qt0);
-    half8 kb[D / 16], vb[D / 16];
-    f.grows(kb, K, k0 + 32 * lo, 0u);
-    f.grows(vb, V, k0 + 32 * lo, 0u);
-    put(0);
-    f.flip(kb, qsign);
-    int s = 0;
-    for (int qt = qt0; qt < T; ++qt) {
-        barrier();  // query tile qt is in stage s; every wave is done with qt-1
-        const bool more = qt + 1 < T;
-        if (more) fetch(qt + 1);
-        const _Float16* Qs = stage_of(s);
-        const _Float16* Os = Qs + G::TILE;
-        const float* fl = reinterpret_cast<const float*>(Qs + 2 * G::TILE);
+        barrier_dma();
         const int q0 = qt * 64 + 32 * hi;  // first query row of this wave
 
-        // Every LDS read of the products is issued before the first of them,
-        // the row values first: with one wave per SIMD nothing else hides
-        // their latency.  Register r of a score block holds query
-        // q0 + 8(r/4) + 4g + r%4 for key k0 + 32lo + n.
-        float4 l4[4], d4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            l4[j] = *reinterpret_cast<const float4*>(fl + 32 * hi + 8 * j + 4 * g);
-            d4[j] = *reinterpret_cast<const float4*>(fl + 64 + 32 * hi + 8 * j + 4 * g);
-        }
-        half8 aq[D / 16], ao[D / 16];
-        f.rows(aq, Qs, 32 * hi);
-        f.rows(ao, Os, 32 * hi);
-        __builtin_amdgcn_sched_barrier(0);
+        // S and dP: register r of a score block holds query
+        // q0 + 8(r/4) + 4g + r%4 for key k0 + 32lo + n
         floatx16 sacc, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = dp[r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(aq[kk], kb[kk], sacc, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(ao[kk], vb[kk], dp, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(row1(Qs, 32 * hi, kk), row1(Ks, 32 * lo, kk),
+                                                          sacc, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(row1(Os, 32 * hi, kk), row1(Vs, 32 * lo, kk),
+                                                        dp, 0, 0, 0);
         }
-        // the dO columns of dV += P^T dO go out while the scores are formed,
-        // the Q columns of dK += dS^T Q before the dV products
-        half8 bo[2][NB], bq[2][NB];
-        f.cols(bo, Os, 32 * hi);
-        __builtin_amdgcn_sched_barrier(0);
-        const int key = k0 + 32 * lo + n;
         half8 pa[2], sa[2];
         // only the diagonal tile and tiles that reach past S need the mask
         const bool edge = (CAUSAL && qt == kt) || qt * 64 + 64 > S || k0 + 64 > S;
-        if (edge) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qrow = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
-                const float lse_r = l4[r >> 2][r & 3], dlt_r = d4[r >> 2][r & 3];
-                const bool vis = qrow < S && key < S && (!CAUSAL || key <= qrow);
-                const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -lse_r)) : 0.f;
-                pa[r >> 3][r & 7] = (_Float16)p;
-                sa[r >> 3][r & 7] = (_Float16)(p * (dp[r] - dlt_r));
-            }
-        } else {
+        for (int j4 = 0; j4 < 4; ++j4) {
+            const float4 l4 = *reinterpret_cast<const float4*>(fl + 32 * hi + 8 * j4 + 4 * g);
+            const float4 d4 = *reinterpret_cast<const float4*>(fl + 64 + 32 * hi + 8 * j4 + 4 * g);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float lse_r = l4[r >> 2][r & 3], dlt_r = d4[r >> 2][r & 3];
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -lse_r));
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * j4 + e;
+                const float lse_r = e == 0 ? l4.x : e == 1 ? l4.y : e == 2 ? l4.z : l4.w;
+                const float dlt_r = e == 0 ? d4.x : e == 1 ? d4.y : e == 2 ? d4.z : d4.w;
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], cs, -lse_r));
+                if (edge) {
+                    const int qrow = q0 + 8 * j4 + 4 * g + e;
+                    const bool vis = qrow < S && key < S && (!CAUSAL || key <= qrow);
+                    p = vis ? p : 0.f;
+                }
                 pa[r >> 3][r & 7] = (_Float16)p;
                 sa[r >> 3][r & 7] = (_Float16)(p * (dp[r] - dlt_r));
             }
         }
-        f.cols(bq, Qs, 32 * hi);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-                dv[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bo[h][b], pa[h], dv[b], 0, 0, 0);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-                dk[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bq[h][b], sa[h], dk[b], 0, 0, 0);
-        if (more) put(s ^ 1);
-        s ^= 1;
+            for (int b = 0; b < NB; ++b) {
+                dv[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(col1(Os, 32 * hi, h, b), pa[h], dv[b], 0, 0, 0);
+                dk[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(col1(Qs, 32 * hi, h, b), sa[h], dk[b], 0, 0, 0);
+            }
     }
 
     // The two query halves (hi = 0, 1) hold partial sums over disjoint rows.
@@ -173,7 +190,7 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     // each adding the other's partial (a + b, the same in either order), and
     // stores its rows from registers.  Register r of block b: head dim
     // 32b + 8(r/4) + 4g + r%4 of key k0 + 32lo + n.
-    barrier();
+    barrier_dma();
     {
         float4* mine = reinterpret_cast<float4*>(lds) + (2 * lo + hi) * (NB * 4) * 64;
         if (hi == 0) {
@@ -184,7 +201,7 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
             for (int b = 0; b < NB; ++b) f.give(mine, dk[b], b);
         }
     }
-    barrier();
+    barrier_dma();
     {
         const float4* other = reinterpret_cast<const float4*>(lds) + (2 * lo + (hi ^ 1)) * (NB * 4) * 64;
         if (hi == 0) {
@@ -195,7 +212,6 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
             for (int b = 0; b < NB; ++b) f.take(dv[b], other, b);
         }
     }
-    const int key = k0 + 32 * lo + n;
     if (hi == 0) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) f.store_block(dK, dk[b], key, b, scale);
@@ -213,8 +229,7 @@ hipError_t launch_dkdv_t(const BwdArgs& a) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), grid, dim3(256), 0, (hipStream_t)a.stream,
                        (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,
                        (const _Float16*)a.dout, (const float*)a.workspace, a.lse,
-                       (_Float16*)a.dk, (_Float16*)a.dv, BH, a.S, bwd_c(a.scale), a.scale,
-                       bwd_qsign(a.scale));
+                       (_Float16*)a.dk, (_Float16*)a.dv, BH, a.S, a.scale * kLog2e, a.scale);
     return hipGetLastError();
 }
 
