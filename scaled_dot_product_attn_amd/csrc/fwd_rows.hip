@@ -8,7 +8,8 @@
 // GPU", section "Ground rules": one fused kernel instead of a pipeline of
 // kernels through global workspaces).
 //
-// Work split.  Wave w takes query rows 32w .. 32w+31 of the tile and walks
+// Work split.  Wave w takes query rows 32r .. 32r+31 of the tile (r = w, or
+// 3 - w in the workgroups with odd u, below) and walks
 // the keys in 32-key chunks; the four waves share every staged chunk, so a
 // K/V byte brought into LDS feeds 128 query rows (half the global->LDS bytes
 // per FLOP of a 64-row tile), and since no wave splits the keys of its rows
@@ -110,7 +111,8 @@ struct Rows {
     size_t base, lse_base;
     float c;
     uint32_t qsign;
-    int lane, g, n, w;
+    // w: the wave (its share of every load); wr: its 32-row group of the tile
+    int lane, g, n, w, wr;
 
     // Buffer over rows r0 .. min(r0 + rows, S) - 1 of t: reads past them
     // return zero (an empty buffer when r0 >= S).  r0 is uniform;
@@ -256,12 +258,12 @@ struct Rows {
     template <bool STEADY>
     __device__ void run(int qt, int nk, bool issued, int nxt, int nk_nxt) {
         const int q0 = qt * G::BM;
-        const int row = q0 + 32 * w + n;
+        const int row = q0 + 32 * wr + n;
         // last key this lane's row may see
         const int vis = CAUSAL ? min(row, S - 1) : S - 1;
         // this wave's last chunk: the one holding its rows' diagonal (or the
         // last key); every key of the earlier ones is visible to all its rows
-        const int cw = CAUSAL ? min(q0 + 32 * w, S - 1) / G::BN : nk - 1;
+        const int cw = CAUSAL ? min(q0 + 32 * wr, S - 1) / G::BN : nk - 1;
 
         // prologue: K(0), Q, V(0), K(1) into their slots; wait for K(0) and
         // Q, barrier; the Q fragments (sign-flipped for a negative scale) and
@@ -284,7 +286,7 @@ struct Rows {
         asm volatile("" ::: "memory");
         half8 qf[D / 16];
         {
-            const int qrow = 32 * w + n;
+            const int qrow = 32 * wr + n;
             const _Float16* qp = sl.q + qrow * D;
             const int sw = swz_k(qrow);
 #pragma unroll
@@ -438,6 +440,13 @@ fwd_rows_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     f.g = f.lane >> 5;
     f.n = f.lane & 31;
     f.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // odd u: row groups in reverse order.  Under causal masking the wave with
+    // row group r idles after its diagonal chunk for 3 - r chunks; the
+    // dispatcher gives every CU one workgroup of the grid's first half and
+    // one of its second, i.e. u and u+1 of a head when the grid fills the
+    // chip once, with wave w of each on SIMD w: reversed, each SIMD gets one
+    // early- and one late-finishing wave
+    f.wr = (u & 1) ? 3 - f.w : f.w;
     const int nk0 = ((CAUSAL ? min(S, (qt0 + 1) * G::BM) : S) + G::BN - 1) / G::BN;
     const bool two = PAIRED && u != qt0;
     const int nk1 = (min(S, (u + 1) * G::BM) + G::BN - 1) / G::BN;
