@@ -82,6 +82,28 @@ def test_splitkv_repeat_bit_identical(gpu):
         assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
 
 
+def test_splitkv_shared_workspace(gpu):
+    """D = 512: one workspace, left as the previous call wrote it, serves
+    calls of different shapes and split counts in turn, and each gives the
+    bytes of a call on a workspace of its own: no call reads what it did not
+    write in that call."""
+    import torch
+    shapes = [(1, 8, 1024, True, 3), (2, 3, 300, True, 4), (1, 2, 333, False, 16),
+              (1, 8, 1024, True, 7), (1, 1, 65, True, 2)]
+    need = max(gpu.splitkv_workspace_bytes(B, H, S, 512, c, sp) for B, H, S, c, sp in shapes)
+    shared = torch.full((need,), 0x7f, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for i, (B, H, S, causal, splits) in enumerate(shapes):
+            log(f"shared workspace rep={rep} B={B} H={H} S={S} causal={causal} splits={splits}")
+            q, k, v = (to_dev(rnd(1300 + 10 * i + t, (B, H, S, 512), 0.5)) for t in range(3))
+            scale = float(np.float32(1 / np.sqrt(512)))
+            o1, l1 = gpu.fwd_splitkv(q, k, v, causal=causal, scale=scale, splits=splits,
+                                     workspace=shared)
+            o2, l2 = gpu.fwd_splitkv(q, k, v, causal=causal, scale=scale, splits=splits)
+            torch.cuda.synchronize()
+            assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 # D = 64, 128: workloads 1 and 2, every split count from 1 to one chunk per
 # 64-key tile, and the default
 @pytest.mark.parametrize("c", [1, 2])
