@@ -99,6 +99,23 @@ def test_batch_heads_layout(gpu, oracle_mod, D):
         check(o, lse, o_ref, l_ref, f"B3 H5 S77 D{D} causal={causal}")
 
 
+@pytest.mark.parametrize("B,H,S", [(1, 2, 300), (2, 3, 449), (1, 4, 1000), (1, 1, 65),
+                                   (1, 3, 576)])
+def test_d512_causal_tile_counts(gpu, oracle_mod, B, H, S):
+    """D = 512 causal at odd and even counts of 64-row query tiles, ragged
+    last tiles and several heads: every row against the oracle, and the
+    call's bytes repeat."""
+    shape = (B, H, S, 512)
+    q, k, v = (rnd(13_000 + S + H + t, shape) for t in range(3))
+    sc = 1 / math.sqrt(512)
+    log(f"D=512 causal B={B} H={H} S={S}")
+    o, lse = run(gpu, q, k, v, True, sc)
+    o_ref, l_ref = oracle_mod.attn_fwd(q, k, v, True, sc)
+    check(o, lse, o_ref, l_ref, f"D=512 causal B={B} H={H} S={S}")
+    o2, lse2 = run(gpu, q, k, v, True, sc)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
 # ---------------------------------- grids of more than one wave of workgroups
 
 # More 64-row query tiles than 2 x 256 (two workgroups on each of the 256
