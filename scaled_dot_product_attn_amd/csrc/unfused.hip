@@ -11,8 +11,10 @@
 // transposed LDS reads of V, only the place where S and P live differs.
 //
 //   qk_kernel      S[b,h,i,j] = scale * q_i . k_j           (fp32, row stride Sp)
-//   softmax_kernel P[b,h,i,j] = exp(S - max) / sum  (fp16),  LSE = max + log(sum)
-//   pv_kernel      O = P V                                  (fp16 out)
+//   softmax_reg_kernel (rows up to 4096 entries; softmax_kernel beyond)
+//                  P[b,h,i,j] = exp(S - max) / sum  (fp16),  LSE = max + log(sum)
+//   pv_stream_kernel (D = 64, 128; pv_kernel at D = 512)
+//                  O = P V                                  (fp16 out)
 //
 // Workspace: S (fp32) then P (fp16), both [B, H, S, Sp] with Sp = S rounded up
 // to 64, so every row starts 128-byte aligned.  Under causal masking only the
@@ -206,6 +208,75 @@ softmax_kernel(const float* __restrict__ Sm, _Float16* __restrict__ P, float* __
     if (lane == 0) LSE[rowid] = (m + __builtin_amdgcn_logf(l)) * kLn2;
 }
 
+// One wave per row with the whole row in registers, for rows of up to 512 NG
+// entries: lane L holds entries 8(L + 64t) .. +7 for t < NG.  S is read once
+// (two 16-byte loads per group, all in flight together), the row max and sum
+// are wave reductions, and P goes out in 16-byte stores.
+template <int NG>
+__global__ void __launch_bounds__(256)
+softmax_reg_kernel(const float* __restrict__ Sm, _Float16* __restrict__ P, float* __restrict__ LSE,
+                   int BHS, int S, int Sp, int causal)
+{
+    const int rowid = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (rowid >= BHS) return;
+    const int lane = threadIdx.x & 63;
+    const int i = rowid % S;
+    const int L = causal ? i + 1 : S;  // visible keys
+    // P columns written, as softmax_kernel: zeros past the diagonal up to the
+    // next multiple of 128 (the P V kernel reads whole tiles)
+    const int Lp = causal ? min(Sp, ((i + 128) / 128) * 128) : Sp;
+    const float* srow = Sm + (size_t)rowid * Sp;
+    _Float16* prow = P + (size_t)rowid * Sp;
+    float x[NG][8];
+#pragma unroll
+    for (int t = 0; t < NG; ++t) {
+        const int j = 8 * (lane + 64 * t);
+        float4 a = {kNegInf, kNegInf, kNegInf, kNegInf}, b = a;
+        if (j < L) {
+            a = *reinterpret_cast<const float4*>(srow + j);
+            b = *reinterpret_cast<const float4*>(srow + j + 4);
+        }
+        x[t][0] = a.x, x[t][1] = a.y, x[t][2] = a.z, x[t][3] = a.w;
+        x[t][4] = b.x, x[t][5] = b.y, x[t][6] = b.z, x[t][7] = b.w;
+    }
+    // base-2 logits, -inf past the visible keys; the row max
+    float m = kNegInf;
+#pragma unroll
+    for (int t = 0; t < NG; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            x[t][e] = 8 * (lane + 64 * t) + e < L ? x[t][e] * kLog2e : kNegInf;
+            m = fmaxf(m, x[t][e]);
+        }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    // every row sees key 0, so m is finite
+    float l = 0.f;
+#pragma unroll
+    for (int t = 0; t < NG; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) l += __builtin_amdgcn_exp2f(x[t][e] - m);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off, 64);
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int t = 0; t < NG; ++t) {
+        const int j = 8 * (lane + 64 * t);
+        if (j < Lp) {
+            u32x4 pk;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float p0 = __builtin_amdgcn_exp2f(x[t][2 * h] - m) * inv;
+                const float p1 = __builtin_amdgcn_exp2f(x[t][2 * h + 1] - m) * inv;
+                pk[h] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)p0) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)p1) << 16);
+            }
+            *reinterpret_cast<u32x4*>(prow + j) = pk;
+        }
+    }
+    if (lane == 0) LSE[rowid] = (m + __builtin_amdgcn_logf(l)) * kLn2;
+}
+
 // ---------------------------------------------------------------- P V
 
 template <int D>
@@ -313,6 +384,121 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
     }
     if (qrow < S) {
         _Float16* orow = O + vbase + (size_t)qrow * D + G::DW * dq;
+#pragma unroll
+        for (int b = 0; b < G::DW / 32; ++b)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                u32x2 pk;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const _Float16 lo = (_Float16)o[b][4 * q4 + 2 * h];
+                    const _Float16 hi = (_Float16)o[b][4 * q4 + 2 * h + 1];
+                    pk[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+                }
+                *reinterpret_cast<u32x2*>(orow + 32 * b + 8 * q4 + 4 * g) = pk;
+            }
+    }
+}
+
+// P V for D = 64, 128 (one 32-row group of every wave, BM = 128 queries per
+// workgroup), streaming: the V rows and P fragments of key tiles t+1 and t+2
+// are in flight while tile t's products run (three register sets, the loop
+// unrolled by three so that each set has a fixed name).  Workgroup order:
+// (batch, head) fastest, so that a head's query tiles land on one XCD (heads
+// are dealt round-robin to the XCDs when B*H is a multiple of 8) and share
+// its V in that XCD's L2; under causal masking the heaviest query tiles
+// first across all heads (keeping a head's tiles back to back on its XCD
+// instead cut the re-reads but cost more in balance than it saved).
+template <int D>
+__global__ void __launch_bounds__(256, D == 64 ? 2 : 1)
+pv_stream_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V,
+                 _Float16* __restrict__ O, int BH, int S, int Sp, int causal)
+{
+    using G = PvGeo<D>;
+    static_assert(G::DQ == 1 && G::BM == 128, "one 32-row group per wave");
+    __shared__ __attribute__((aligned(1024))) _Float16 vs[G::BN * D];
+    const int TQ = (S + G::BM - 1) / G::BM;
+    const int bh = blockIdx.x % BH, u = blockIdx.x / BH;
+    const int qt = causal ? TQ - 1 - u : u;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int g = lane >> 5, n = lane & 31;
+    const int q0 = qt * G::BM;
+    const int qrow = q0 + 32 * w + n;
+    const size_t vbase = (size_t)bh * S * D;
+    const _Float16* prow = P + ((size_t)bh * S + min(qrow, S - 1)) * Sp + 8 * g;
+    const int kend = causal ? min(S, q0 + G::BM) : S;
+    const int nT = (kend + G::BN - 1) / G::BN;
+
+    floatx16 o[G::DW / 32];
+#pragma unroll
+    for (int b = 0; b < G::DW / 32; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
+
+    // V rows of key tile t (bounds-checked: zeros past S) and this lane's P
+    // fragments of it: its query, keys 16ks + 8g .. +7 (P is written up to
+    // the workgroup's last tile end)
+    auto load = [&](int t, u32x4* st, half8* pf) {
+        const int j0 = t * G::BN;
+        const auto r = rsrc(V + vbase + (size_t)j0 * D, (uint32_t)min(S - j0, G::BN) * D * 2);
+#pragma unroll
+        for (int c = 0; c < G::CH; ++c)
+            st[c] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (tid + 256 * c), 0, 0));
+#pragma unroll
+        for (int ks = 0; ks < G::BN / 16; ++ks)
+            pf[ks] = *reinterpret_cast<const half8*>(prow + j0 + 16 * ks);
+    };
+    const int n16 = n >> 4, jj = n & 15;
+    const int sub = (jj & 3) >> 1, half = jj & 1;
+    const int sw = swz_pv<D>(jj >> 2);  // (row & 3) == jj >> 2 for every row read
+    auto step = [&](const u32x4* st, const half8* pf) {
+#pragma unroll
+        for (int c = 0; c < G::CH; ++c) {
+            const int ci = tid + 256 * c, row = ci / G::CPR, cc = ci % G::CPR;
+            *reinterpret_cast<u32x4*>(vs + row * D + 8 * (cc ^ swz_pv<D>(row))) = st[c];
+        }
+        barrier();
+        // transposed reads deliver keys 16ks + 8g + 4tt + 0..3, the lane's P keys
+        const _Float16* rowp = vs + (8 * g + (jj >> 2)) * D + 4 * half;
+#pragma unroll
+        for (int ks = 0; ks < G::BN / 16; ++ks)
+#pragma unroll
+            for (int b = 0; b < G::DW / 32; ++b) {
+                const int logical = 4 * b + 2 * n16 + sub;
+                const _Float16* pb = rowp + 8 * (logical ^ sw) + 16 * ks * D;
+                half4 part[2];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+                    part[tt] = __builtin_bit_cast(
+                        half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_half4*)(pb + 4 * tt * D)));
+                const half8 a = {part[0][0], part[0][1], part[0][2], part[0][3],
+                                 part[1][0], part[1][1], part[1][2], part[1][3]};
+                o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], o[b], 0, 0, 0);
+            }
+        barrier();
+    };
+    // Loads past the last tile re-read the last tile (unused): issuing every
+    // load unconditionally keeps the wait counts exact, so the products of
+    // tile t wait for tile t's loads only.
+    u32x4 s0[G::CH], s1[G::CH], s2[G::CH];
+    half8 f0[G::BN / 16], f1[G::BN / 16], f2[G::BN / 16];
+    const int last = nT - 1;
+    load(0, s0, f0);
+    load(min(1, last), s1, f1);
+    for (int t = 0; t < nT; t += 3) {
+        load(min(t + 2, last), s2, f2);
+        step(s0, f0);
+        if (t + 1 >= nT) break;
+        load(min(t + 3, last), s0, f0);
+        step(s1, f1);
+        if (t + 2 >= nT) break;
+        load(min(t + 4, last), s1, f1);
+        step(s2, f2);
+    }
+    if (qrow < S) {
+        _Float16* orow = O + vbase + (size_t)qrow * D;
 #pragma unroll
         for (int b = 0; b < G::DW / 32; ++b)
 #pragma unroll
@@ -485,13 +671,29 @@ hipError_t launch_unfused(const FwdArgs& a, void* workspace) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int BHS = BH * S;
-    hipLaunchKernelGGL(softmax_kernel, dim3((unsigned)((BHS + 3) / 4)), dim3(256), 0, st, Sm, P, a.lse,
-                       BHS, S, Sp, a.causal);
+    const dim3 sm_grid((unsigned)((BHS + 3) / 4));
+    // rows of up to 4096 entries are held in registers
+    if (Sp <= 512)
+        hipLaunchKernelGGL(softmax_reg_kernel<1>, sm_grid, dim3(256), 0, st, Sm, P, a.lse, BHS, S, Sp, a.causal);
+    else if (Sp <= 1024)
+        hipLaunchKernelGGL(softmax_reg_kernel<2>, sm_grid, dim3(256), 0, st, Sm, P, a.lse, BHS, S, Sp, a.causal);
+    else if (Sp <= 2048)
+        hipLaunchKernelGGL(softmax_reg_kernel<4>, sm_grid, dim3(256), 0, st, Sm, P, a.lse, BHS, S, Sp, a.causal);
+    else if (Sp <= 4096)
+        hipLaunchKernelGGL(softmax_reg_kernel<8>, sm_grid, dim3(256), 0, st, Sm, P, a.lse, BHS, S, Sp, a.causal);
+    else
+        hipLaunchKernelGGL(softmax_kernel, sm_grid, dim3(256), 0, st, Sm, P, a.lse, BHS, S, Sp, a.causal);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.D == 64) return launch_pv<64>(a, P, Sp);
-    if (a.D == 128) return launch_pv<128>(a, P, Sp);
-    return launch_pv<512>(a, P, Sp);
+    if (a.D == 512) return launch_pv<512>(a, P, Sp);
+    const dim3 pv_grid((unsigned)(BH * ((a.S + 127) / 128)));
+    if (a.D == 64)
+        hipLaunchKernelGGL(pv_stream_kernel<64>, pv_grid, dim3(256), 0, st, P, (const _Float16*)a.v,
+                           (_Float16*)a.o, BH, S, Sp, a.causal);
+    else
+        hipLaunchKernelGGL(pv_stream_kernel<128>, pv_grid, dim3(256), 0, st, P, (const _Float16*)a.v,
+                           (_Float16*)a.o, BH, S, Sp, a.causal);
+    return hipGetLastError();
 }
 
 }  // namespace attn

@@ -35,6 +35,20 @@ def test_unfused_ragged(gpu, oracle_mod, D, causal):
         check(o, lse, o_ref, l_ref, f"unfused S={S} D={D} causal={causal}")
 
 
+@pytest.mark.parametrize("S,D,causal", [(700, 64, True), (1500, 128, False), (2900, 64, True),
+                                         (4200, 64, True)])
+def test_unfused_long_rows(gpu, oracle_mod, S, D, causal):
+    """Rows of every length class of the softmax step: held in registers in
+    groups of up to 1024, 2048 and 4096 entries, and longer rows (two passes
+    over S).  Every row of one head against the oracle."""
+    log(f"unfused long rows S={S} D={D} causal={causal}")
+    q, k, v = (rnd(31_000 + S + D + t, (1, 1, S, D)) for t in range(3))
+    sc = 1 / math.sqrt(D)
+    o, lse = run(gpu, q, k, v, causal, sc, unfused=True)
+    o_ref, l_ref = oracle_mod.attn_fwd(q, k, v, causal, sc)
+    check(o, lse, o_ref, l_ref, f"unfused S={S} D={D} causal={causal}")
+
+
 def test_unfused_matches_fused(gpu):
     """The two paths differ only in where S lives: their outputs agree to fp16
     rounding (well inside the gate)."""
