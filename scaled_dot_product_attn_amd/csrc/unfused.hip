@@ -43,13 +43,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // 64-key tiles), the heaviest query tiles first under causal masking, walking
 // the key tiles of its chunk that the tile's rows see.  Wave
 // (wq, wk): query rows 32wq .. +31 against keys 32wk .. +31 of every key
-// tile.  Its Q fragments stay in registers and the next tile's K fragments
-// are loaded while the current tile's products and stores run, so the
-// kernel streams S out instead of waiting on a load per 64 x 64 block.
+// tile.  The query rows and then each key tile come in as whole rows (each
+// thread a run of contiguous 16-byte chunks, bounds-checked), go through an
+// XOR-swizzled LDS tile and are read back as MFMA fragments: loading the
+// fragments straight from global memory, 16 bytes per lane across 32 rows,
+// requested every 128-byte line four times and ran ~15% slower.  The Q
+// fragments stay in registers; the next two key tiles' loads are in flight
+// while the current tile's products and stores run.
 // DC head dims starting at d0 are reduced; ACC adds into S instead of
 // writing.  Under causal masking only the blocks holding some j <= i are
 // stored (the softmax reads no other entry).
-constexpr int kQkChunk = 4;
+constexpr int kQkChunk = 8;
 
 template <int DC, bool ACC>
 __global__ void __launch_bounds__(256)
@@ -71,19 +75,37 @@ qk_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     const int g = lane >> 5, n = lane & 31;
     const int wq = w & 1, wk = w >> 1;
     const size_t base = (size_t)bh * S * D;
-    const int qrow = min(qt * 64 + 32 * wq + n, S - 1);  // A operand row (query)
     half8 qf[NK];
-    {
-        const _Float16* qp = Q + base + (size_t)qrow * D + d0 + 8 * g;
+    // key tile t: its 64 rows (DC head dims from d0) loaded as contiguous
+    // 16-byte chunks per thread, bounds-checked (zeros past S), staged in
+    // registers, then written to the LDS tile with the chunk index XOR-ed by
+    // the row's swizzle; the B operand fragments are read from there
+    constexpr int CPR = DC / 8;               // 16-byte chunks per K row
+    constexpr int CH = 64 * CPR / 256;        // chunks per thread per tile
+    __shared__ __attribute__((aligned(1024))) _Float16 kt[64 * DC];
+    auto swz = [](int r) { return CPR == 16 ? (r & 15) : CPR == 8 ? ((r >> 1) & 7) : (r & 31); };
+    auto load_k = [&](int t, u32x4* st) {
+        const int j0 = t * 64;
+        const auto r = rsrc(K + base + (size_t)j0 * D, (uint32_t)max(0, min(S - j0, 64)) * D * 2);
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk) qf[kk] = *reinterpret_cast<const half8*>(qp + 16 * kk);
-    }
-    // B operand column (key) fragments of key tile t
-    auto load_k = [&](int t, half8* kf) {
-        const int krow = min(t * 64 + 32 * wk + n, S - 1);
-        const _Float16* kp = K + base + (size_t)krow * D + d0 + 8 * g;
+        for (int c = 0; c < CH; ++c) {
+            const int ci = threadIdx.x + 256 * c, row = ci / CPR, cc = ci % CPR;
+            st[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                r, (row * D + d0 + 8 * cc) * 2, 0, 0));
+        }
+    };
+    auto put_k = [&](const u32x4* st) {
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk) kf[kk] = *reinterpret_cast<const half8*>(kp + 16 * kk);
+        for (int c = 0; c < CH; ++c) {
+            const int ci = threadIdx.x + 256 * c, row = ci / CPR, cc = ci % CPR;
+            *reinterpret_cast<u32x4*>(kt + row * DC + 8 * (cc ^ swz(row))) = st[c];
+        }
+    };
+    auto frag_k = [&](half8* kf) {
+        const int kr = 32 * wk + n;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+            kf[kk] = *reinterpret_cast<const half8*>(kt + kr * DC + 8 * ((2 * kk + g) ^ swz(kr)));
     };
     const int i0 = qt * 64 + 32 * wq;  // first query row of the wave
     // the wave's 32 x 32 fp32 block goes out through LDS, so that every
@@ -127,14 +149,49 @@ qk_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
         wait_lgkm0();
         __builtin_amdgcn_wave_barrier();
     };
-    half8 ka[NK], kb[NK];
-    load_k(kt0, ka);
-    for (int t = kt0; t < kt0 + nkt; t += 2) {
-        if (t + 1 < kt0 + nkt) load_k(t + 1, kb);
-        block(t, ka);
-        if (t + 1 >= kt0 + nkt) break;
-        if (t + 2 < kt0 + nkt) load_k(t + 2, ka);
-        block(t + 1, kb);
+    // one LDS tile: put (after the previous step's reads, barrier), read the
+    // fragments (barrier), products and stores; the next tiles' loads in
+    // flight meanwhile (issued unconditionally, past the chunk re-reading its
+    // last tile, so that the wait counts are exact)
+    auto step = [&](int t, const u32x4* st) {
+        put_k(st);
+        barrier();
+        half8 kf[NK];
+        frag_k(kf);
+        barrier();
+        block(t, kf);
+    };
+    u32x4 sa[CH], sb[CH], sc[CH];
+    const int last = kt0 + nkt - 1;
+    {
+        // the query tile's rows through the same LDS tile, as the A operand
+        const int j0 = qt * 64;
+        const auto r = rsrc(Q + base + (size_t)j0 * D, (uint32_t)max(0, min(S - j0, 64)) * D * 2);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int ci = threadIdx.x + 256 * c, row = ci / CPR, cc = ci % CPR;
+            sa[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                r, (row * D + d0 + 8 * cc) * 2, 0, 0));
+        }
+        put_k(sa);
+        barrier();
+        const int qr = 32 * wq + n;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+            qf[kk] = *reinterpret_cast<const half8*>(kt + qr * DC + 8 * ((2 * kk + g) ^ swz(qr)));
+        barrier();
+    }
+    load_k(kt0, sa);
+    load_k(min(kt0 + 1, last), sb);
+    for (int t = kt0; t <= last; t += 3) {
+        load_k(min(t + 2, last), sc);
+        step(t, sa);
+        if (t + 1 > last) break;
+        load_k(min(t + 3, last), sa);
+        step(t + 1, sb);
+        if (t + 2 > last) break;
+        load_k(min(t + 4, last), sb);
+        step(t + 2, sc);
     }
 }
 
@@ -418,6 +475,7 @@ pv_stream_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V,
     using G = PvGeo<D>;
     static_assert(G::DQ == 1 && G::BM == 128, "one 32-row group per wave");
     __shared__ __attribute__((aligned(1024))) _Float16 vs[G::BN * D];
+    __shared__ __attribute__((aligned(1024))) _Float16 ps[G::BM * G::BN];
     const int TQ = (S + G::BM - 1) / G::BM;
     const int bh = blockIdx.x % BH, u = blockIdx.x / BH;
     const int qt = causal ? TQ - 1 - u : u;
@@ -426,7 +484,6 @@ pv_stream_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V,
     const int q0 = qt * G::BM;
     const int qrow = q0 + 32 * w + n;
     const size_t vbase = (size_t)bh * S * D;
-    const _Float16* prow = P + ((size_t)bh * S + min(qrow, S - 1)) * Sp + 8 * g;
     const int kend = causal ? min(S, q0 + G::BM) : S;
     const int nT = (kend + G::BN - 1) / G::BN;
 
@@ -436,10 +493,15 @@ pv_stream_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V,
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
 
-    // V rows of key tile t (bounds-checked: zeros past S) and this lane's P
-    // fragments of it: its query, keys 16ks + 8g .. +7 (P is written up to
-    // the workgroup's last tile end)
-    auto load = [&](int t, u32x4* st, half8* pf) {
+    // V rows of key tile t (bounds-checked: zeros past S) and the tile's
+    // 128 x 64 block of P (written up to the workgroup's last tile end), both
+    // as contiguous 16-byte chunks per thread; P goes through an XOR-swizzled
+    // LDS tile (16-byte fragment reads across 32 rows straight from global
+    // memory requested every line four times)
+    // P rows q0 .. q0 + 127 of the tile (rows past S read zero)
+    const auto prs = rsrc(P + ((size_t)bh * S + q0) * Sp, (uint32_t)min(S - q0, G::BM) * Sp * 2);
+    auto swzp = [](int r) { return (r >> 1) & 7; };
+    auto load = [&](int t, u32x4* st, u32x4* pc) {
         const int j0 = t * G::BN;
         const auto r = rsrc(V + vbase + (size_t)j0 * D, (uint32_t)min(S - j0, G::BN) * D * 2);
 #pragma unroll
@@ -447,19 +509,34 @@ pv_stream_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V,
             st[c] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (tid + 256 * c), 0, 0));
 #pragma unroll
-        for (int ks = 0; ks < G::BN / 16; ++ks)
-            pf[ks] = *reinterpret_cast<const half8*>(prow + j0 + 16 * ks);
+        for (int c = 0; c < 4; ++c) {
+            const int ci = tid + 256 * c, row = ci >> 3, cc = ci & 7;
+            pc[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                prs, (row * Sp + j0 + 8 * cc) * 2, 0, 0));
+        }
     };
     const int n16 = n >> 4, jj = n & 15;
     const int sub = (jj & 3) >> 1, half = jj & 1;
     const int sw = swz_pv<D>(jj >> 2);  // (row & 3) == jj >> 2 for every row read
-    auto step = [&](const u32x4* st, const half8* pf) {
+    auto step = [&](const u32x4* st, const u32x4* pc) {
 #pragma unroll
         for (int c = 0; c < G::CH; ++c) {
             const int ci = tid + 256 * c, row = ci / G::CPR, cc = ci % G::CPR;
             *reinterpret_cast<u32x4*>(vs + row * D + 8 * (cc ^ swz_pv<D>(row))) = st[c];
         }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int ci = tid + 256 * c, row = ci >> 3, cc = ci & 7;
+            *reinterpret_cast<u32x4*>(ps + row * G::BN + 8 * (cc ^ swzp(row))) = pc[c];
+        }
         barrier();
+        half8 pf[G::BN / 16];
+        {
+            const int pr = 32 * w + n;
+#pragma unroll
+            for (int ks = 0; ks < G::BN / 16; ++ks)
+                pf[ks] = *reinterpret_cast<const half8*>(ps + pr * G::BN + 8 * ((2 * ks + g) ^ swzp(pr)));
+        }
         // transposed reads deliver keys 16ks + 8g + 4tt + 0..3, the lane's P keys
         const _Float16* rowp = vs + (8 * g + (jj >> 2)) * D + 4 * half;
 #pragma unroll
@@ -483,7 +560,7 @@ pv_stream_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V,
     // load unconditionally keeps the wait counts exact, so the products of
     // tile t wait for tile t's loads only.
     u32x4 s0[G::CH], s1[G::CH], s2[G::CH];
-    half8 f0[G::BN / 16], f1[G::BN / 16], f2[G::BN / 16];
+    u32x4 f0[4], f1[4], f2[4];
     const int last = nT - 1;
     load(0, s0, f0);
     load(min(1, last), s1, f1);
