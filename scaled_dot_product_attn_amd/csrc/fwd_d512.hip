@@ -383,22 +383,15 @@ struct Fwd512 {
         const int row = q0 + 32 * rg + n;
         const int vis = causal ? min(row, S - 1) : S - 1;  // last key this lane's row sees
 
-        // Q^T fragment of this wave's rows and head-dim half.
-        half8 qf[G::DH / 16];
-        {
-            const u32x4* src = reinterpret_cast<const u32x4*>(
-                Q + base + (size_t)min(row, S - 1) * G::D + G::DH * dh);
-#pragma unroll
-            for (int kk = 0; kk < G::DH / 16; ++kk) {
-                u32x4 x = src[2 * kk + g];
-                x ^= qsign;
-                qf[kk] = __builtin_bit_cast(half8, x);
-                // held in accumulation registers, which the matrix
-                // instructions read their B operand from directly: the
-                // ordinary registers go to O, the scores and the fragments
-                asm volatile("" : "+a"(qf[kk]));
-            }
-        }
+        // The tile's 64 query rows go through the two V stages (free until
+        // the first V tile) as whole 1 KB rows, swizzled like K rows, and
+        // this wave's Q^T fragments are read from there.  Loading the
+        // fragments straight from global memory (16 bytes per lane across 32
+        // rows, four instructions per 128-byte line, 64 KB per workgroup in
+        // flight at once) thrashed the vector L1 cache.  Rows past S read
+        // zero (their outputs are not stored).
+        dma(Q, vs(0), 2 * qt, true);
+        dma(Q, vs(1), 2 * qt + 1, true);
 
         float m = kNegInf, l = 0.f;
         floatx16 o[NB];
@@ -420,6 +413,23 @@ struct Fwd512 {
             barrier_dma_but8();
         } else {
             barrier_dma();
+        }
+        // Q^T fragment of this wave's rows and head-dim half (rows 32 rg + n
+        // of the two stages), the sign of a negative scale applied
+        half8 qf[G::DH / 16];
+        {
+            const _Float16* qp = vs(0) + (32 * rg + n) * G::D;
+            const int x = (32 * dh + g) ^ swz_k512(n);
+#pragma unroll
+            for (int kk = 0; kk < G::DH / 16; ++kk) {
+                u32x4 v = *reinterpret_cast<const u32x4*>(qp + 8 * (x ^ (2 * kk)));
+                v ^= qsign;
+                qf[kk] = __builtin_bit_cast(half8, v);
+                // held in accumulation registers, which the matrix
+                // instructions read their B operand from directly: the
+                // ordinary registers go to O, the scores and the fragments
+                asm volatile("" : "+a"(qf[kk]));
+            }
         }
         floatx16 s_cur = qk_half<false>(qf, 0);
         publish(xch(), s_cur);
