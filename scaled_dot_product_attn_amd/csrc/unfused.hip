@@ -360,6 +360,9 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
 {
     using G = PvGeo<D>;
     __shared__ __attribute__((aligned(1024))) _Float16 vs[G::BN * D];
+    __shared__ __attribute__((aligned(1024))) _Float16 ps[G::BM * G::BN];
+    constexpr int PCH = G::BM * G::BN / 8 / 256;  // 16-byte P chunks per thread per tile
+    static_assert(PCH >= 1, "whole P tile per pass");
     const int TQ = (S + G::BM - 1) / G::BM;
     const int bh = blockIdx.x / TQ, qt = blockIdx.x % TQ;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -368,7 +371,9 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
     const int q0 = qt * G::BM;
     const int qrow = q0 + 32 * qg + n;
     const size_t vbase = (size_t)bh * S * D;
-    const _Float16* prow = P + ((size_t)bh * S + min(qrow, S - 1)) * Sp + 8 * g;
+    // the P rows q0 .. q0 + BM - 1 of the workgroup (rows past S read zero)
+    const auto prs = rsrc(P + ((size_t)bh * S + q0) * Sp, (uint32_t)min(S - q0, G::BM) * Sp * 2);
+    auto swzp = [](int r) { return (r >> 1) & 7; };
     const int kend = causal ? min(S, q0 + G::BM) : S;
     const int nT = (kend + G::BN - 1) / G::BN;
 
@@ -378,7 +383,10 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
 
-    u32x4 st[G::CH];
+    // V rows and the BM x BN block of P of key tile t, as contiguous 16-byte
+    // chunks per thread (P once per workgroup, through an XOR-swizzled LDS
+    // tile: every wave of a query group reads the same P fragments)
+    u32x4 st[G::CH], pc[PCH];
     auto load = [&](int t) {
         const int j0 = t * G::BN;
         const auto r = rsrc(V + vbase + (size_t)j0 * D, (uint32_t)min(S - j0, G::BN) * D * 2);
@@ -386,6 +394,12 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
         for (int u = 0; u < G::CH; ++u)
             st[u] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (tid + 256 * u), 0, 0));
+#pragma unroll
+        for (int c = 0; c < PCH; ++c) {
+            const int ci = tid + 256 * c, row = ci >> 3, cc = ci & 7;
+            pc[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                prs, (row * Sp + j0 + 8 * cc) * 2, 0, 0));
+        }
     };
     auto store = [&]() {
 #pragma unroll
@@ -393,27 +407,32 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
             const int ci = tid + 256 * u, row = ci / G::CPR, cc = ci % G::CPR;
             *reinterpret_cast<u32x4*>(vs + row * D + 8 * (cc ^ swz_pv<D>(row))) = st[u];
         }
+#pragma unroll
+        for (int c = 0; c < PCH; ++c) {
+            const int ci = tid + 256 * c, row = ci >> 3, cc = ci & 7;
+            *reinterpret_cast<u32x4*>(ps + row * G::BN + 8 * (cc ^ swzp(row))) = pc[c];
+        }
     };
 
     const int n16 = n >> 4, jj = n & 15;
     const int sub = (jj & 3) >> 1, half = jj & 1;
     const int sw = swz_pv<D>(jj >> 2);  // (row & 3) == jj >> 2 for every row read
-    // P^T operands of a key tile: this lane's query, keys j0 + 16ks + 8g .. +7,
-    // loaded a tile ahead of their products
-    half8 pcur[G::BN / 16], pnext[G::BN / 16];
-    auto load_p = [&](int t, half8* pf) {
-#pragma unroll
-        for (int ks = 0; ks < G::BN / 16; ++ks)
-            pf[ks] = *reinterpret_cast<const half8*>(prow + t * G::BN + 16 * ks);
-    };
+    // the next tile's loads go out after this tile's stores to LDS,
+    // unconditionally (past the last tile re-reading it) so that the wait
+    // counts stay exact
     load(0);
-    load_p(0, pcur);
     for (int t = 0; t < nT; ++t) {
         store();
         barrier();
-        if (t + 1 < nT) {
-            load(t + 1);
-            load_p(t + 1, pnext);
+        load(min(t + 1, nT - 1));
+        // P^T operands: this lane's query, keys 16ks + 8g .. +7 of the tile
+        half8 pcur[G::BN / 16];
+        {
+            const int pr = 32 * qg + n;
+#pragma unroll
+            for (int ks = 0; ks < G::BN / 16; ++ks)
+                pcur[ks] = *reinterpret_cast<const half8*>(ps + pr * G::BN +
+                                                           8 * ((2 * ks + g) ^ swzp(pr)));
         }
         // transposed reads deliver keys 16ks + 8g + 4tt + 0..3: the lane's 8 keys
         // are contiguous, matching a 16-byte load of its P row
@@ -436,8 +455,6 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
             }
         }
         barrier();
-#pragma unroll
-        for (int ks = 0; ks < G::BN / 16; ++ks) pcur[ks] = pnext[ks];
     }
     if (qrow < S) {
         _Float16* orow = O + vbase + (size_t)qrow * D + G::DW * dq;
