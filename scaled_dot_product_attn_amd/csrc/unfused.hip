@@ -336,9 +336,9 @@ softmax_reg_kernel(const float* __restrict__ Sm, _Float16* __restrict__ P, float
 
 // ---------------------------------------------------------------- P V
 
-template <int D>
+template <int D, int DWX = (D < 128 ? D : 128)>
 struct PvGeo {
-    static constexpr int DW = D < 128 ? D : 128;   // output dims per wave
+    static constexpr int DW = DWX;                 // output dims per wave
     static constexpr int DQ = D / DW;              // waves sharing a query group
     static constexpr int QG = 4 / DQ;              // 32-query groups per workgroup
     static constexpr int BM = 32 * QG;             // queries per workgroup
@@ -475,8 +475,9 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
     }
 }
 
-// P V for D = 64, 128 (one 32-row group of every wave, BM = 128 queries per
-// workgroup), streaming: the V rows and P fragments of key tiles t+1 and t+2
+// P V for D = 64, 128 with DW output dims per wave (DW = D: four 32-row
+// groups, 128 queries per workgroup; DW = D/2: two 32-row groups of two
+// waves each, 64 queries), streaming: the V rows and P fragments of key tiles t+1 and t+2
 // are in flight while tile t's products run (three register sets, the loop
 // unrolled by three so that each set has a fixed name).  Workgroup order:
 // (batch, head) fastest, so that a head's query tiles land on one XCD (heads
@@ -484,22 +485,28 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
 // its V in that XCD's L2; under causal masking the heaviest query tiles
 // first across all heads (keeping a head's tiles back to back on its XCD
 // instead cut the re-reads but cost more in balance than it saved).
-template <int D>
-__global__ void __launch_bounds__(256, D == 64 ? 2 : 1)
+template <int D, int DW>
+__global__ void __launch_bounds__(256, (D == 64 || DW < D) ? 2 : 1)
 pv_stream_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V,
                  _Float16* __restrict__ O, int BH, int S, int Sp, int causal)
 {
-    using G = PvGeo<D>;
-    static_assert(G::DQ == 1 && G::BM == 128, "one 32-row group per wave");
+    using G = PvGeo<D, DW>;
+    constexpr int PCH = G::BM * G::BN / 8 / 256;  // 16-byte P chunks per thread per tile
     __shared__ __attribute__((aligned(1024))) _Float16 vs[G::BN * D];
     __shared__ __attribute__((aligned(1024))) _Float16 ps[G::BM * G::BN];
     const int TQ = (S + G::BM - 1) / G::BM;
     const int bh = blockIdx.x % BH, u = blockIdx.x / BH;
-    const int qt = causal ? TQ - 1 - u : u;
+    // causal, 128-row tiles (one workgroup per CU): heaviest first.  64-row
+    // tiles (two per CU): the heavy half of the tiles in the first half of
+    // the grid and the light half in the second, so that the two workgroups
+    // a CU receives carry about T+1 tiles of work between them.
+    const int qt = !causal ? u : G::BM == 128 ? TQ - 1 - u
+                                              : (u < TQ / 2 ? TQ - 1 - u : u - TQ / 2);
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 5, n = lane & 31;
+    const int qg = w / G::DQ, dq = w % G::DQ;
     const int q0 = qt * G::BM;
-    const int qrow = q0 + 32 * w + n;
+    const int qrow = q0 + 32 * qg + n;
     const size_t vbase = (size_t)bh * S * D;
     const int kend = causal ? min(S, q0 + G::BM) : S;
     const int nT = (kend + G::BN - 1) / G::BN;
@@ -526,7 +533,7 @@ pv_stream_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V,
             st[c] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (tid + 256 * c), 0, 0));
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < PCH; ++c) {
             const int ci = tid + 256 * c, row = ci >> 3, cc = ci & 7;
             pc[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                 prs, (row * Sp + j0 + 8 * cc) * 2, 0, 0));
@@ -542,14 +549,14 @@ pv_stream_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V,
             *reinterpret_cast<u32x4*>(vs + row * D + 8 * (cc ^ swz_pv<D>(row))) = st[c];
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < PCH; ++c) {
             const int ci = tid + 256 * c, row = ci >> 3, cc = ci & 7;
             *reinterpret_cast<u32x4*>(ps + row * G::BN + 8 * (cc ^ swzp(row))) = pc[c];
         }
         barrier();
         half8 pf[G::BN / 16];
         {
-            const int pr = 32 * w + n;
+            const int pr = 32 * qg + n;
 #pragma unroll
             for (int ks = 0; ks < G::BN / 16; ++ks)
                 pf[ks] = *reinterpret_cast<const half8*>(ps + pr * G::BN + 8 * ((2 * ks + g) ^ swzp(pr)));
@@ -560,7 +567,7 @@ pv_stream_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V,
         for (int ks = 0; ks < G::BN / 16; ++ks)
 #pragma unroll
             for (int b = 0; b < G::DW / 32; ++b) {
-                const int logical = 4 * b + 2 * n16 + sub;
+                const int logical = (G::DW * dq) / 8 + 4 * b + 2 * n16 + sub;
                 const _Float16* pb = rowp + 8 * (logical ^ sw) + 16 * ks * D;
                 half4 part[2];
 #pragma unroll
@@ -577,7 +584,7 @@ pv_stream_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V,
     // load unconditionally keeps the wait counts exact, so the products of
     // tile t wait for tile t's loads only.
     u32x4 s0[G::CH], s1[G::CH], s2[G::CH];
-    u32x4 f0[4], f1[4], f2[4];
+    u32x4 f0[PCH], f1[PCH], f2[PCH];
     const int last = nT - 1;
     load(0, s0, f0);
     load(min(1, last), s1, f1);
@@ -592,7 +599,7 @@ pv_stream_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V,
         step(s2, f2);
     }
     if (qrow < S) {
-        _Float16* orow = O + vbase + (size_t)qrow * D;
+        _Float16* orow = O + vbase + (size_t)qrow * D + G::DW * dq;
 #pragma unroll
         for (int b = 0; b < G::DW / 32; ++b)
 #pragma unroll
@@ -780,13 +787,14 @@ hipError_t launch_unfused(const FwdArgs& a, void* workspace) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.D == 512) return launch_pv<512>(a, P, Sp);
-    const dim3 pv_grid((unsigned)(BH * ((a.S + 127) / 128)));
+    // 64-row tiles, two workgroups per CU
+    const dim3 pv_grid((unsigned)(BH * ((a.S + 63) / 64)));
     if (a.D == 64)
-        hipLaunchKernelGGL(pv_stream_kernel<64>, pv_grid, dim3(256), 0, st, P, (const _Float16*)a.v,
-                           (_Float16*)a.o, BH, S, Sp, a.causal);
+        hipLaunchKernelGGL((pv_stream_kernel<64, 32>), pv_grid, dim3(256), 0, st, P,
+                           (const _Float16*)a.v, (_Float16*)a.o, BH, S, Sp, a.causal);
     else
-        hipLaunchKernelGGL(pv_stream_kernel<128>, pv_grid, dim3(256), 0, st, P, (const _Float16*)a.v,
-                           (_Float16*)a.o, BH, S, Sp, a.causal);
+        hipLaunchKernelGGL((pv_stream_kernel<128, 64>), pv_grid, dim3(256), 0, st, P,
+                           (const _Float16*)a.v, (_Float16*)a.o, BH, S, Sp, a.causal);
     return hipGetLastError();
 }
 
