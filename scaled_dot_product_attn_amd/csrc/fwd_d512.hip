@@ -614,29 +614,51 @@ merge512_kernel(const float* __restrict__ ws, _Float16* __restrict__ O, float* _
     const int r = rb * kMergeRows + (threadIdx.x >> 5);  // row within the query tile
     const int d0 = 16 * (threadIdx.x & 31);
     const int row = qt * G::BM + r;
+    // Chunks in groups of four, every load of a group issued before any is
+    // used (the chunk order of the sums unchanged).
     float mt = kNegInf;
-    for (int cc = 0; cc < nch; ++cc) mt = fmaxf(mt, slot0[cc * kSlotFloats + kSlotOFloats + r]);
+    for (int c0 = 0; c0 < nch; c0 += 4) {
+        float mv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            mv[j] = c0 + j < nch ? slot0[(c0 + j) * kSlotFloats + kSlotOFloats + r] : kNegInf;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mt = fmaxf(mt, mv[j]);
+    }
     // O = sum_c w_c l_c (O_c / l_c) / sum_c w_c l_c with w_c = 2^(m_c - m*);
     // a chunk that saw no key of this row has l = 0 (and a zero O_c / l_c)
     float lsum = 0.f;
     float4 acc[4] = {};
-    for (int cc = 0; cc < nch; ++cc) {
-        const float* sl = slot0 + cc * kSlotFloats;
-        const float wl = __builtin_amdgcn_exp2f(sl[kSlotOFloats + r] - mt) *
-                         sl[kSlotOFloats + G::BM + r];
-        lsum += wl;
-        const u32x4* x = reinterpret_cast<const u32x4*>(
-            reinterpret_cast<const _Float16*>(sl) + (size_t)r * G::D + d0);
+    for (int c0 = 0; c0 < nch; c0 += 4) {
+        float mv[4], lv[4];
+        u32x4 xv[4][2];
 #pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
-            const half8 y = __builtin_bit_cast(half8, x[e2]);
+        for (int j = 0; j < 4; ++j) {
+            // chunks past the last re-read it (unused)
+            const float* sl = slot0 + min(c0 + j, nch - 1) * kSlotFloats;
+            mv[j] = sl[kSlotOFloats + r];
+            lv[j] = sl[kSlotOFloats + G::BM + r];
+            const u32x4* x = reinterpret_cast<const u32x4*>(
+                reinterpret_cast<const _Float16*>(sl) + (size_t)r * G::D + d0);
+            xv[j][0] = x[0];
+            xv[j][1] = x[1];
+        }
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                float4& a = acc[2 * e2 + e];
-                a.x += wl * (float)y[4 * e];
-                a.y += wl * (float)y[4 * e + 1];
-                a.z += wl * (float)y[4 * e + 2];
-                a.w += wl * (float)y[4 * e + 3];
+        for (int j = 0; j < 4; ++j) {
+            if (c0 + j >= nch) break;
+            const float wl = __builtin_amdgcn_exp2f(mv[j] - mt) * lv[j];
+            lsum += wl;
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+                const half8 y = __builtin_bit_cast(half8, xv[j][e2]);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    float4& a = acc[2 * e2 + e];
+                    a.x += wl * (float)y[4 * e];
+                    a.y += wl * (float)y[4 * e + 1];
+                    a.z += wl * (float)y[4 * e + 2];
+                    a.w += wl * (float)y[4 * e + 3];
+                }
             }
         }
     }
