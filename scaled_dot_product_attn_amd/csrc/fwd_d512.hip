@@ -53,12 +53,19 @@ namespace {
 
 using namespace detail;
 
-struct G512 {
+// NW waves: NW/2 row groups of 32 query rows, each split over two head-dim
+// halves.  NW = 4: 64-row tiles (the split-KV units and large grids);
+// NW = 2: 32-row tiles (fused calls with few tiles: twice the workgroups,
+// and per key tile half the fragment reads and exchange traffic through the
+// CU's LDS, the tile fills being the same).
+template <int NW_>
+struct G512T {
     static constexpr int D = 512;
     static constexpr int DH = 256;               // head dims per sub-tile
-    static constexpr int NW = 4;
+    static constexpr int NW = NW_;
+    static constexpr int RG = NW / 2;            // 32-row groups per workgroup
     static constexpr int NT = 64 * NW;
-    static constexpr int BM = 64;                // query rows per workgroup
+    static constexpr int BM = 32 * RG;           // query rows per workgroup
     static constexpr int BN = 32;                // keys per tile
     static constexpr int NB = DH / 32;           // 32-dim output blocks of a wave
     static constexpr int TILE = BN * D;          // halfs of a K or V stage (swizzled rows, no pad)
@@ -66,8 +73,10 @@ struct G512 {
     static constexpr int XCH = NW * 16 * 64;     // floats of the S^T exchange buffer
     // two K stages, two V stages and the exchange buffer
     static constexpr int LDS_BYTES = 4 * TILE * 2 + XCH * 4;
+    static_assert(NW == 2 || NW == 4, "row groups");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
+using G512 = G512T<4>;
 
 // K row swizzle: 16-byte chunk index XOR (row & 15).  Every 1 KB row starts on
 // the same bank, so without it the 16 rows that a group of 16 lanes reads at
@@ -83,8 +92,9 @@ __device__ __forceinline__ int swz_v512(int r) { return 4 * (r & 3); }
 constexpr size_t kSlotOFloats = (size_t)G512::BM * G512::D / 2;
 constexpr size_t kSlotFloats = kSlotOFloats + 2 * G512::BM;
 
+template <int NW>
 struct Fwd512 {
-    using G = G512;
+    using G = G512T<NW>;
     static constexpr int NB = G::NB;
     const _Float16* __restrict__ Q;
     const _Float16* __restrict__ K;
@@ -154,11 +164,13 @@ struct Fwd512 {
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     }
-    // The same, with this wave's last ROWS (= 8) tile-row loads still in
+    // The same, with this wave's last ROWS (8 or 16) tile-row loads still in
     // flight (loads complete in issue order).
     __device__ __forceinline__ void barrier_dma_but8() const {
-        static_assert(G::ROWS == 8, "vmcnt immediate");
-        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+        if constexpr (G::ROWS == 8)
+            asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     }
@@ -202,7 +214,11 @@ struct Fwd512 {
             for (int e = 0; e < 4; ++e) {
                 acc[e & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[k4 & 1][e], qf[4 * k4 + e],
                                                                     acc[e & 1], 0, 0, 0);
-                if (DMA && (e & 1)) dma_row(r, ks(dn), 2 * k4 + (e >> 1), true, ln);
+                if constexpr (G::ROWS == 8) {
+                    if (DMA && (e & 1)) dma_row(r, ks(dn), 2 * k4 + (e >> 1), true, ln);
+                } else {
+                    if (DMA) dma_row(r, ks(dn), 4 * k4 + e, true, ln);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -219,7 +235,7 @@ struct Fwd512 {
                 float4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
     }
     __device__ __forceinline__ void add_partner(const float* x, floatx16& s) const {
-        const float* other = x + (w ^ 2) * 16 * 64;
+        const float* other = x + (w ^ G::RG) * 16 * 64;  // (rg, 1 - dh)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const float4 p = *reinterpret_cast<const float4*>(other + (4 * q4) * 64 + 4 * lane);
@@ -315,8 +331,10 @@ struct Fwd512 {
 #pragma unroll
             for (int h = 0; h < 2; ++h)
                 o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[b % 3][h], pf[h], o[b], 0, 0, 0);
-            // row b of this wave's share of V tile jv into V stage dv
-            dma_row(rv, vs(dv), b, false, ln);
+            // rows of this wave's share of V tile jv into V stage dv
+#pragma unroll
+            for (int u = b * G::ROWS / NB; u < (b + 1) * G::ROWS / NB; ++u)
+                dma_row(rv, vs(dv), u, false, ln);
 #pragma unroll
             for (int r = 2 * b; r < 2 * b + 2; ++r) {
                 float t = __builtin_fmaf(s[r], c, -m);
@@ -390,8 +408,8 @@ struct Fwd512 {
         // rows, four instructions per 128-byte line, 64 KB per workgroup in
         // flight at once) thrashed the vector L1 cache.  Rows past S read
         // zero (their outputs are not stored).
-        dma(Q, vs(0), 2 * qt, true);
-        dma(Q, vs(1), 2 * qt + 1, true);
+#pragma unroll
+        for (int h = 0; h < G::RG; ++h) dma(Q, vs(h), G::RG * qt + h, true);
 
         float m = kNegInf, l = 0.f;
         floatx16 o[NB];
@@ -473,7 +491,8 @@ struct Fwd512 {
         // Epilogue: both waves of a row group hold the same m and l; each
         // writes its 256 output dims.
         const float lt = sum_halves(l);
-        if (part) {
+        // (partial states: 64-row split-KV units only)
+        if (NW == 4 && part) {
             // the chunk's own normalised output O / l in fp16 (|O / l| <=
             // max |V|; 0 where the chunk saw no key of the row), then m, l
             const float pinv = lt > 0.f ? 1.0f / lt : 0.f;
@@ -553,24 +572,37 @@ struct Chunking {
 
 
 
-__global__ void __launch_bounds__(256, 1)
+// NW = 4: one workgroup per (batch, head, 64-row tile, key chunk) of ch.
+// NW = 2: one per (batch, head, 32-row tile), all of its keys, heaviest
+// tiles first under causal masking (ch, U and ws unused).
+template <int NW>
+__global__ void __launch_bounds__(64 * NW, 1)
 fwd512_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
               const _Float16* __restrict__ V, _Float16* __restrict__ O,
               float* __restrict__ LSE, int BH, int S, int causal, float c, uint32_t qsign,
               Chunking ch, int U, float* __restrict__ ws)
 {
-    using G = G512;
+    using G = G512T<NW>;
     __shared__ __attribute__((aligned(1024))) _Float16 lds[G::LDS_BYTES / 2];
 
     const int bh = blockIdx.x % BH;
     const int unit = blockIdx.x / BH;
-    int qt, chunk;
-    ch.decode(unit, qt, chunk);
-    const int n = ch.nkt(qt);
-    const int kt0 = chunk * ch.C, kt1 = min(n, kt0 + ch.C);
-    float* part = ch.nchunks(qt) > 1 ? ws + ((size_t)bh * U + unit) * kSlotFloats : nullptr;
+    int qt, kt0 = 0, kt1;
+    float* part = nullptr;
+    if constexpr (NW == 4) {
+        int chunk;
+        ch.decode(unit, qt, chunk);
+        const int n = ch.nkt(qt);
+        kt0 = chunk * ch.C;
+        kt1 = min(n, kt0 + ch.C);
+        if (ch.nchunks(qt) > 1) part = ws + ((size_t)bh * U + unit) * kSlotFloats;
+    } else {
+        const int T = (S + G::BM - 1) / G::BM;
+        qt = causal ? T - 1 - unit : unit;
+        kt1 = ((causal ? min(S, (qt + 1) * G::BM) : S) + G::BN - 1) / G::BN;
+    }
 
-    Fwd512 f;
+    Fwd512<NW> f;
     f.Q = Q;
     f.K = K;
     f.V = V;
@@ -587,8 +619,8 @@ fwd512_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     f.lane = threadIdx.x & 63;
     f.g = f.lane >> 5;
     f.n = f.lane & 31;
-    f.rg = f.w & 1;
-    f.dh = f.w >> 1;
+    f.rg = f.w % G::RG;
+    f.dh = f.w / G::RG;
     f.run(qt, kt0, kt1, part);
 }
 
@@ -680,6 +712,9 @@ merge512_kernel(const float* __restrict__ ws, _Float16* __restrict__ O, float* _
     if (d0 == 0) LSE[(size_t)bh * S + row] = (mt + __builtin_amdgcn_logf(lsum)) * kLn2;
 }
 
+// Fused calls with fewer 64-row tiles than this run on 32-row tiles.
+constexpr long long kFew512 = 256;
+
 Chunking make_chunking(int S, int causal, int splits) {
     Chunking ch;
     ch.S = S;
@@ -697,7 +732,17 @@ hipError_t launch(const FwdArgs& a, int splits, float* ws) {
     const int BH = a.B * a.H;
     const float c = fabsf(a.scale) * 1.44269504088896340736f;
     const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
-    hipLaunchKernelGGL(fwd512_kernel, dim3((unsigned)((long long)U * BH)), dim3(G::NT), 0,
+    if (splits <= 0 && (long long)BH * ch.T < kFew512) {
+        // few 64-row tiles: 32-row tiles of two waves, twice the workgroups
+        using G2 = G512T<2>;
+        const long long T2 = (a.S + G2::BM - 1) / G2::BM;
+        hipLaunchKernelGGL(fwd512_kernel<2>, dim3((unsigned)(T2 * BH)), dim3(G2::NT), 0,
+                           (hipStream_t)a.stream,
+                           (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,
+                           (_Float16*)a.o, a.lse, BH, a.S, a.causal, c, qsign, ch, U, ws);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(fwd512_kernel<4>, dim3((unsigned)((long long)U * BH)), dim3(G::NT), 0,
                        (hipStream_t)a.stream,
                        (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,
                        (_Float16*)a.o, a.lse, BH, a.S, a.causal, c, qsign, ch, U, ws);

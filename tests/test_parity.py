@@ -116,6 +116,29 @@ def test_d512_causal_tile_counts(gpu, oracle_mod, B, H, S):
     assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
 
 
+def test_d512_many_tiles(gpu, oracle_mod):
+    """D = 512 fused with at least 256 tiles of 64 rows (B2 H8 S1024, causal
+    and not): the 64-row, four-wave form (fewer tiles take 32-row tiles of
+    two waves); sampled heads against the oracle, and the bytes equal a
+    split-KV call with one split (the same kernel, one chunk per tile)."""
+    import torch
+    B, H, S, D = 2, 8, 1024, 512
+    assert B * H * (S // 64) >= 256
+    q, k, v = (rnd(14_000 + t, (B, H, S, D), 0.5) for t in range(3))
+    sc = float(np.float32(1 / math.sqrt(D)))
+    for causal in (True, False):
+        log(f"D=512 many tiles causal={causal}")
+        o, lse = run(gpu, q, k, v, causal, sc)
+        for b, h in ((0, 0), (1, 7), (1, 3)):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            o_ref, l_ref = oracle_mod.attn_fwd(q[sl], k[sl], v[sl], causal, sc)
+            check(o[sl], lse[sl], o_ref, l_ref, f"D=512 B2 H8 S1024 causal={causal} b={b} h={h}")
+        o1, l1 = gpu.fwd_splitkv(to_dev(q), to_dev(k), to_dev(v), causal=causal, scale=sc,
+                                 splits=1)
+        torch.cuda.synchronize()
+        assert np.array_equal(o1.cpu().numpy(), o) and np.array_equal(l1.cpu().numpy(), lse)
+
+
 # ---------------------------------- grids of more than one wave of workgroups
 
 # More 64-row query tiles than 2 x 256 (two workgroups on each of the 256
