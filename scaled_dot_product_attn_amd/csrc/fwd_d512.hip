@@ -10,8 +10,10 @@
 // nonlinear, so merging softmax(S_0)V and softmax(S_1)V afterwards would be
 // wrong.  Here the two sub-tiles live in two different waves:
 //
-//   * A workgroup (4 waves) owns 64 query rows.  Wave w handles row group
-//     rg = w & 1 (32 rows) and head-dim half dh = w >> 1 (256 dims).
+//   * A workgroup of NW waves owns 32 NW/2 query rows: 64 rows with four
+//     waves (split-KV units, fused calls with many tiles), 32 rows with two
+//     (fused calls with few tiles).  Wave w handles row group
+//     rg = w % (NW/2) (32 rows) and head-dim half dh = w / (NW/2) (256 dims).
 //   * Per 32-key tile, wave (rg, dh) computes the partial S^T over its 256
 //     dims (16 v_mfma_f32_32x32x16_f16), publishes it in LDS, and after the
 //     next barrier adds its partner's (rg, 1-dh) partial: both waves then
