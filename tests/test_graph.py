@@ -16,7 +16,11 @@ def _inputs(seed, shape, n):
                   for t in range(3)) for i in range(n)]
 
 
-@pytest.mark.parametrize("path", ["fused", "unfused", "decode", "splitkv"])
+# fused: the 64-row D = 128 kernel; fused_rows: the 128-row kernel with
+# tiles in pairs (>= 512 pairs of 128-row tiles); fused512: D = 512 on
+# 32-row tiles of two waves
+@pytest.mark.parametrize("path", ["fused", "fused_rows", "fused512", "unfused", "decode",
+                                  "splitkv"])
 def test_graph_replays_match_eager(gpu, path):
     import torch
     if path == "decode":
@@ -32,6 +36,15 @@ def test_graph_replays_match_eager(gpu, path):
         ws = torch.empty(gpu.splitkv_workspace_bytes(B, H, S, D, causal, splits),
                          dtype=torch.uint8, device="cuda")
         qshape = (B, H, S, D)
+    elif path == "fused_rows":
+        B, H, S, D, causal, sc = 1, 512, 200, 128, True, 0.088
+        assert B * H * ((-(-S // 128) + 1) // 2) >= 512
+        sets = _inputs(94_000, (B, H, S, D), 3)
+        qshape = (B, H, S, D)
+    elif path == "fused512":
+        B, H, S, D, causal, sc = 1, 2, 300, 512, True, 0.044
+        sets = _inputs(95_000, (B, H, S, D), 3)
+        qshape = (B, H, S, D)
     else:
         B, H, S, D, causal, sc = 2, 3, 300, 128, True, 0.088
         sets = _inputs(91_000, (B, H, S, D), 3)
@@ -43,7 +56,7 @@ def test_graph_replays_match_eager(gpu, path):
     def call(i):
         q, k, v = sets[i]
         o, lse = outs[i]
-        if path == "fused":
+        if path in ("fused", "fused_rows", "fused512"):
             gpu.fwd(q, k, v, causal=causal, scale=sc, out=o, lse=lse)
         elif path == "unfused":
             gpu.fwd_unfused(q, k, v, causal=causal, scale=sc, out=o, lse=lse, workspace=ws)
