@@ -635,13 +635,13 @@ constexpr int kMergeRows = 8;
 
 __global__ void __launch_bounds__(256)
 merge512_kernel(const float* __restrict__ ws, _Float16* __restrict__ O, float* __restrict__ LSE,
-                int BH, int S, Chunking ch, int U)
+                int BH, int S, Chunking ch, int U, int qt_first)
 {
     using G = G512;
     const int per_tile = G::BM / kMergeRows;
     const int bh = blockIdx.x % BH;
     const int rest = blockIdx.x / BH;
-    const int qt = rest / per_tile, rb = rest % per_tile;
+    const int qt = qt_first + rest / per_tile, rb = rest % per_tile;
     const int nch = ch.nchunks(qt);
     if (nch <= 1) return;  // written directly by the first kernel
     const float* slot0 = ws + ((size_t)bh * U + ch.first_unit(qt)) * kSlotFloats;
@@ -750,9 +750,12 @@ hipError_t launch(const FwdArgs& a, int splits, float* ws) {
                        (_Float16*)a.o, a.lse, BH, a.S, a.causal, c, qsign, ch, U, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || U == ch.T) return e;  // no query tile was split
-    const long long merge_blocks = (long long)ch.T * (G::BM / kMergeRows) * BH;
+    // the split tiles are qt_first .. T-1 (a tile's key count grows with qt)
+    int qt_first = 0;
+    while (ch.nchunks(qt_first) <= 1) ++qt_first;
+    const long long merge_blocks = (long long)(ch.T - qt_first) * (G::BM / kMergeRows) * BH;
     hipLaunchKernelGGL(merge512_kernel, dim3((unsigned)merge_blocks), dim3(256), 0,
-                       (hipStream_t)a.stream, ws, (_Float16*)a.o, a.lse, BH, a.S, ch, U);
+                       (hipStream_t)a.stream, ws, (_Float16*)a.o, a.lse, BH, a.S, ch, U, qt_first);
     return hipGetLastError();
 }
 
