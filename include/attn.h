@@ -35,7 +35,8 @@
  *   - Deterministic: the same inputs give the same output bytes (no atomics,
  *     fixed reduction order).  The kernel depends on the whole call: at
  *     D = 128 a call with B*H*ceil(S/128) >= 512 query tiles of 128 rows
- *     runs the 128-row kernel, a smaller one the 64-row kernel, so a (b, h)
+ *     (>= 256 when not causal) runs the 128-row kernel, a smaller one the
+ *     64-row kernel, so a (b, h)
  *     slice of a large call launched on its own agrees with its slice of the
  *     call to rounding (both within the parity gate), bit for bit only when
  *     both calls take the same kernel.

@@ -85,11 +85,13 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     if (st != ATTN_OK) return st;
     const attn::FwdArgs a{q, k, v, o, lse, B, H, S, D, causal != 0, scale, stream};
     if (D == 512) return launched(attn::launch_fused_d512(a));
-    // D = 128 with enough 128-row query tiles for two workgroups on every CU
-    // of the 256: the 128-row kernel (half the staged bytes per FLOP, no key
-    // merge); otherwise the 64-row kernel, whose waves split the keys of a
-    // tile and so keep every CU busy on fewer rows
-    if (D == 128 && (long long)B * H * ((S + 127) / 128) >= 512)
+    // D = 128 with enough 128-row query tiles: the 128-row kernel (half the
+    // staged bytes per FLOP, no key merge); otherwise the 64-row kernel,
+    // whose waves split the keys of a tile and so keep every CU busy on fewer
+    // rows.  Enough: causal, two tiles for each of the 256 CUs (with fewer,
+    // the heaviest tiles of the triangle run alone and the 64-row kernel's
+    // heavy/light pairs are faster); non-causal, one per CU (equal tiles).
+    if (D == 128 && (long long)B * H * ((S + 127) / 128) >= (causal ? 512 : 256))
         return launched(attn::launch_fused_rows_d128(a));
     return launched(attn::launch_fused_pipe_d64_d128(a));
 }

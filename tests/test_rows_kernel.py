@@ -1,5 +1,6 @@
 """GPU parity of the D = 128 forward on shapes with many 128-row query tiles
-(B*H*ceil(S/128) >= 512), which attn_fwd runs on the 128-row kernel: four
+(B*H*ceil(S/128) >= 512, or >= 256 when not causal), which attn_fwd runs on
+the 128-row kernel: four
 waves per tile, each owning 32 complete rows, keys in 32-key chunks, the
 causal mask applied on each wave's diagonal chunk only.
 
@@ -27,8 +28,8 @@ def heads_for(S, B=1):
     return -(-512 // (B * t))
 
 
-def routed(B, H, S):
-    return B * H * (-(-S // 128)) >= 512
+def routed(B, H, S, causal=True):
+    return B * H * (-(-S // 128)) >= (512 if causal else 256)
 
 
 def sample_check(oracle_mod, q, k, v, o, lse, causal, sc, what, n_pick=6):
@@ -185,3 +186,18 @@ def test_rows_slice_alone_matches_within_gate(gpu, oracle_mod):
     o2, l2 = run(gpu, q2, k2, v2, True, sc)
     assert np.array_equal(o[:, h:h + 1], o2[:, h:h + 1])
     assert np.array_equal(lse[:, h:h + 1], l2[:, h:h + 1])
+
+
+@pytest.mark.parametrize("B,H,S", [(1, 32, 1024), (1, 128, 200), (2, 8, 2048), (1, 255, 100),
+                                   (1, 256, 100)])
+def test_rows_noncausal_from_256_tiles(gpu, oracle_mod, B, H, S):
+    """Non-causal calls take the 128-row kernel from 256 tiles of 128 rows
+    (one per CU) and the 64-row kernel below: both sides of the boundary,
+    sampled heads against the oracle, and the call's bytes repeat."""
+    log(f"non-causal B={B} H={H} S={S} routed={routed(B, H, S, causal=False)}")
+    q, k, v = (rnd(37_000 + 13 * S + H + t, (B, H, S, D)) for t in range(3))
+    sc = 1 / math.sqrt(D)
+    o, lse = run(gpu, q, k, v, False, sc)
+    sample_check(oracle_mod, q, k, v, o, lse, False, sc, f"non-causal B={B} H={H} S={S}", n_pick=3)
+    o2, lse2 = run(gpu, q, k, v, False, sc)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
