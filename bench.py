@@ -446,7 +446,12 @@ def main():
         for i in range(args.steps):
             step(i)
     end.record(stream)
-    sclk.append(shader_clock_mhz())  # sampled while the timed steps run
+    # the shader clock, sampled every 2 ms until the timed steps end (host
+    # reads of sysfs; the first sample can still show the idle level)
+    sclk.append(shader_clock_mhz())
+    while not end.query():
+        time.sleep(0.002)
+        sclk.append(shader_clock_mhz())
     torch.cuda.synchronize(dev)
     t_wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(end)
@@ -529,6 +534,9 @@ def main():
         "cpu_baseline": None,
     }
     out["sclk_mhz"] = sclk
+    out["sclk_source"] = ("sysfs pp_dpm_sclk level, sampled every 2 ms while the timed steps "
+                          "run; the level ramps over tens of ms, so a ~10 ms run reads low "
+                          "(not the clock the kernels ran at)")
     if args.path == "fused" and args.cold_sets > 0:
         # cold: the calls cycle through cold_sets copies of the inputs, each in
         # its own memory, so that every call's inputs were last touched
