@@ -97,9 +97,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * its intermediates in global memory ("An Optimal Mapper Meets a Real GPU",
  * sections "Ground rules" and "The uncomfortable audit": a multi-kernel
  * pipeline with globally addressed workspaces).
- *   kernel 1: S = scale * Q K^T, fp32 [B, H, S, S] (D = 512: two passes over
- *             the head-dim halves, the second adding into S, as in option 2
- *             of the STAGE_D.md notes);
+ *   kernel 1: S = scale * Q K^T, fp32 [B, H, S, S] (D = 512: one pass over
+ *             all 512 head dims; the two passes of option 2 of the STAGE_D.md
+ *             notes, the second adding into S, measured slower);
  *   kernel 2: P = softmax rows of S, fp16 [B, H, S, S], and LSE;
  *   kernel 3: O = P V.
  * workspace: device memory of at least attn_fwd_unfused_workspace_bytes(B,H,S)

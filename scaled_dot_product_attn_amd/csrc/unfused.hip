@@ -50,12 +50,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // requested every 128-byte line four times and ran ~15% slower.  The Q
 // fragments stay in registers; the next two key tiles' loads are in flight
 // while the current tile's products and stores run.
-// DC head dims starting at d0 are reduced; ACC adds into S instead of
-// writing.  Under causal masking only the blocks holding some j <= i are
+// DC head dims starting at d0 are reduced (D = 512: all of them in one pass;
+// two passes over the halves, the second adding into S, took ~20% longer per
+// ablation or backward call).  Under causal masking only the blocks holding some j <= i are
 // stored (the softmax reads no other entry).
 constexpr int kQkChunk = 8;
 
-template <int DC, bool ACC>
+template <int DC>
 __global__ void __launch_bounds__(256)
 qk_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
           float* __restrict__ Sm, int BH, int S, int Sp, int D, int d0, int causal, float scale)
@@ -137,12 +138,7 @@ qk_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
             // Sp is a multiple of 64 and j of 4: the 4 columns lie in the row
             // (past S they are padding that no kernel reads)
             if (i < S && j < Sp) {
-                float4* dst = reinterpret_cast<float4*>(Sm + ((size_t)bh * S + i) * Sp + j);
-                if (ACC) {
-                    const float4 a = *dst;
-                    v.x += a.x, v.y += a.y, v.z += a.z, v.w += a.w;
-                }
-                *dst = v;
+                *reinterpret_cast<float4*>(Sm + ((size_t)bh * S + i) * Sp + j) = v;
             }
         }
         // the block's LDS reads are done before the next block's writes
@@ -353,24 +349,31 @@ __device__ __forceinline__ int swz_pv(int r) {
     return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3);
 }
 
-template <int D>
-__global__ void __launch_bounds__(256, 1)
+// P V with D output columns per workgroup out of rows of LD (D = LD: whole
+// rows; D < LD: LD / D workgroups per query tile, each owning a column slice
+// of V and O), DWX of them per wave.
+template <int D, int DWX = (D < 128 ? D : 128), int LD = D>
+__global__ void __launch_bounds__(256, LD == D ? 1 : 2)
 pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float16* __restrict__ O,
           int S, int Sp, int causal)
 {
-    using G = PvGeo<D>;
+    using G = PvGeo<D, DWX>;
+    constexpr int NC = LD / D;  // column slices
+    static_assert(NC * D == LD, "whole slices");
     __shared__ __attribute__((aligned(1024))) _Float16 vs[G::BN * D];
     __shared__ __attribute__((aligned(1024))) _Float16 ps[G::BM * G::BN];
     constexpr int PCH = G::BM * G::BN / 8 / 256;  // 16-byte P chunks per thread per tile
     static_assert(PCH >= 1, "whole P tile per pass");
     const int TQ = (S + G::BM - 1) / G::BM;
-    const int bh = blockIdx.x / TQ, qt = blockIdx.x % TQ;
+    const int cs = blockIdx.x % NC, item = blockIdx.x / NC;
+    const int bh = item / TQ, qt = item % TQ;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 5, n = lane & 31;
     const int qg = w / G::DQ, dq = w % G::DQ;
     const int q0 = qt * G::BM;
     const int qrow = q0 + 32 * qg + n;
-    const size_t vbase = (size_t)bh * S * D;
+    const int c0 = cs * D;  // first column of this workgroup's slice
+    const size_t vbase = (size_t)bh * S * LD + c0;
     // the P rows q0 .. q0 + BM - 1 of the workgroup (rows past S read zero)
     const auto prs = rsrc(P + ((size_t)bh * S + q0) * Sp, (uint32_t)min(S - q0, G::BM) * Sp * 2);
     auto swzp = [](int r) { return (r >> 1) & 7; };
@@ -389,11 +392,16 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
     u32x4 st[G::CH], pc[PCH];
     auto load = [&](int t) {
         const int j0 = t * G::BN;
-        const auto r = rsrc(V + vbase + (size_t)j0 * D, (uint32_t)min(S - j0, G::BN) * D * 2);
+        // rows j0 .. of the slice: the last valid row ends inside the range,
+        // the next one starts past it (zeros)
+        const auto r = rsrc(V + vbase + (size_t)j0 * LD,
+                            (uint32_t)(min(S - j0, G::BN) * LD - c0) * 2);
 #pragma unroll
-        for (int u = 0; u < G::CH; ++u)
-            st[u] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (tid + 256 * u), 0, 0));
+        for (int u = 0; u < G::CH; ++u) {
+            const int ci = tid + 256 * u;
+            st[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  r, ((ci / G::CPR) * LD + 8 * (ci % G::CPR)) * 2, 0, 0));
+        }
 #pragma unroll
         for (int c = 0; c < PCH; ++c) {
             const int ci = tid + 256 * c, row = ci >> 3, cc = ci & 7;
@@ -457,7 +465,7 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
         barrier();
     }
     if (qrow < S) {
-        _Float16* orow = O + vbase + (size_t)qrow * D + G::DW * dq;
+        _Float16* orow = O + vbase + (size_t)qrow * LD + G::DW * dq;
 #pragma unroll
         for (int b = 0; b < G::DW / 32; ++b)
 #pragma unroll
@@ -617,14 +625,19 @@ pv_stream_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V,
     }
 }
 
-template <int D>
-hipError_t launch_pv(const FwdArgs& a, const _Float16* P, int Sp) {
-    using G = PvGeo<D>;
-    const int TQ = (a.S + G::BM - 1) / G::BM;
-    hipLaunchKernelGGL(pv_kernel<D>, dim3((unsigned)(a.B * a.H * TQ)), dim3(256), 0,
-                       (hipStream_t)a.stream, P, (const _Float16*)a.v, (_Float16*)a.o, a.S, Sp,
-                       a.causal);
-    return hipGetLastError();
+// O = P V at D = 512 (P: [BH, S, Sp] fp16, V and O: [BH, S, 512]): four
+// workgroups per 64-row query tile, each owning 128 output columns (two waves
+// of 64 per 32-row group).  At B1 H8 S1024 (causal) that is 512 workgroups,
+// two per CU; one workgroup per 32-row tile and all 512 columns gave 256,
+// one per CU, and took 16-22% longer per call in the ablation and the
+// backward.
+void pv512(hipStream_t st, const _Float16* P, const _Float16* V, _Float16* O, int BH, int S,
+           int Sp, int causal) {
+    constexpr int DV = 128, DW = 64;
+    using G = PvGeo<DV, DW>;
+    const int TQ = (S + G::BM - 1) / G::BM;
+    hipLaunchKernelGGL((pv_kernel<DV, DW, 512>), dim3((unsigned)(BH * TQ * (512 / DV))), dim3(256),
+                       0, st, P, V, O, S, Sp, causal);
 }
 
 // ---------------------------------------------------------------- backward, D = 512
@@ -761,13 +774,12 @@ hipError_t launch_unfused(const FwdArgs& a, void* workspace) {
     const _Float16* q = (const _Float16*)a.q;
     const _Float16* k = (const _Float16*)a.k;
     if (a.D == 64)
-        hipLaunchKernelGGL((qk_kernel<64, false>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 64, 0, a.causal, a.scale);
+        hipLaunchKernelGGL((qk_kernel<64>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 64, 0, a.causal, a.scale);
     else if (a.D == 128)
-        hipLaunchKernelGGL((qk_kernel<128, false>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 128, 0, a.causal, a.scale);
+        hipLaunchKernelGGL((qk_kernel<128>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 128, 0, a.causal, a.scale);
     else {
         // two head-dim sub-tiles, summed into S before the softmax
-        hipLaunchKernelGGL((qk_kernel<256, false>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 512, 0, a.causal, a.scale);
-        hipLaunchKernelGGL((qk_kernel<256, true>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 512, 256, a.causal, a.scale);
+        hipLaunchKernelGGL((qk_kernel<512>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 512, 0, a.causal, a.scale);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -786,7 +798,10 @@ hipError_t launch_unfused(const FwdArgs& a, void* workspace) {
         hipLaunchKernelGGL(softmax_kernel, sm_grid, dim3(256), 0, st, Sm, P, a.lse, BHS, S, Sp, a.causal);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.D == 512) return launch_pv<512>(a, P, Sp);
+    if (a.D == 512) {
+        pv512(st, P, (const _Float16*)a.v, (_Float16*)a.o, BH, S, Sp, a.causal);
+        return hipGetLastError();
+    }
     // 64-row tiles, two workgroups per CU
     const dim3 pv_grid((unsigned)(BH * ((a.S + 63) / 64)));
     if (a.D == 64)
@@ -824,10 +839,8 @@ hipError_t launch_bwd512(const BwdArgs& a) {
     const _Float16* dO = (const _Float16*)a.dout;
     const int TQ = (S + 63) / 64;
     const dim3 qk_grid((unsigned)(BH * TQ * ((TQ + kQkChunk - 1) / kQkChunk)));
-    hipLaunchKernelGGL((qk_kernel<256, false>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 512, 0, a.causal, a.scale);
-    hipLaunchKernelGGL((qk_kernel<256, true>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 512, 256, a.causal, a.scale);
-    hipLaunchKernelGGL((qk_kernel<256, false>), qk_grid, dim3(256), 0, st, dO, v, dPm, BH, S, Sp, 512, 0, a.causal, 1.0f);
-    hipLaunchKernelGGL((qk_kernel<256, true>), qk_grid, dim3(256), 0, st, dO, v, dPm, BH, S, Sp, 512, 256, a.causal, 1.0f);
+    hipLaunchKernelGGL((qk_kernel<512>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 512, 0, a.causal, a.scale);
+    hipLaunchKernelGGL((qk_kernel<512>), qk_grid, dim3(256), 0, st, dO, v, dPm, BH, S, Sp, 512, 0, a.causal, 1.0f);
     const int BHS = BH * S;
     hipLaunchKernelGGL(bwd512_delta_kernel, dim3((unsigned)((BHS + 3) / 4)), dim3(256), 0, st, dO,
                        (const _Float16*)a.o, dlt, BHS);
@@ -836,12 +849,9 @@ hipError_t launch_bwd512(const BwdArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // dV = P^T dO, dK = dS^T Q (rows = keys, every column), dQ = dS K (causal rows)
-    using G = PvGeo<512>;
-    const dim3 pv_grid((unsigned)(BH * ((S + G::BM - 1) / G::BM)));
-    hipLaunchKernelGGL(pv_kernel<512>, pv_grid, dim3(256), 0, st, PT, dO, (_Float16*)a.dv, S, Sp, 0);
-    hipLaunchKernelGGL(pv_kernel<512>, pv_grid, dim3(256), 0, st, dST, q, (_Float16*)a.dk, S, Sp, 0);
-    hipLaunchKernelGGL(pv_kernel<512>, pv_grid, dim3(256), 0, st, dS, k, (_Float16*)a.dq, S, Sp,
-                       (int)a.causal);
+    pv512(st, PT, dO, (_Float16*)a.dv, BH, S, Sp, 0);
+    pv512(st, dST, q, (_Float16*)a.dk, BH, S, Sp, 0);
+    pv512(st, dS, k, (_Float16*)a.dq, BH, S, Sp, (int)a.causal);
     return hipGetLastError();
 }
 
