@@ -54,12 +54,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // two passes over the halves, the second adding into S, took ~20% longer per
 // ablation or backward call).  Under causal masking only the blocks holding some j <= i are
 // stored (the softmax reads no other entry).
-constexpr int kQkChunk = 8;
+// Key tiles per workgroup: 8, or at D = 512 the longest of 8, 4 that still
+// makes at least 256 workgroups (one per CU), else 2.  B1 H8 S1024 keeps 8
+// (4: +3.5%); B2 H4 S700 takes 4 (backward 100.0 -> 82.6 us), B2 H3 S449
+// takes 2 (ablation 34.3 -> 22.1 us).
+int qk_chunk(int D, int BH, int TQ) {
+    if (D != 512) return 8;
+    for (int c : {8, 4})
+        if ((long long)BH * TQ * ((TQ + c - 1) / c) >= 256) return c;
+    return 2;
+}
 
 template <int DC>
 __global__ void __launch_bounds__(256)
 qk_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
-          float* __restrict__ Sm, int BH, int S, int Sp, int D, int d0, int causal, float scale)
+          float* __restrict__ Sm, int BH, int S, int Sp, int D, int d0, int causal, float scale,
+          int kQkChunk)
 {
     constexpr int NK = DC / 16;
     const int TQ = (S + 63) / 64;
@@ -769,17 +779,18 @@ hipError_t launch_unfused(const FwdArgs& a, void* workspace) {
     float* Sm = reinterpret_cast<float*>(workspace);
     _Float16* P = reinterpret_cast<_Float16*>(Sm + (size_t)BH * S * Sp);
     const int TQ = (S + 63) / 64;
+    const int kQkChunk = qk_chunk(a.D, BH, TQ);
     const dim3 qk_grid((unsigned)(BH * TQ * ((TQ + kQkChunk - 1) / kQkChunk)));
     const hipStream_t st = (hipStream_t)a.stream;
     const _Float16* q = (const _Float16*)a.q;
     const _Float16* k = (const _Float16*)a.k;
     if (a.D == 64)
-        hipLaunchKernelGGL((qk_kernel<64>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 64, 0, a.causal, a.scale);
+        hipLaunchKernelGGL((qk_kernel<64>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 64, 0, a.causal, a.scale, kQkChunk);
     else if (a.D == 128)
-        hipLaunchKernelGGL((qk_kernel<128>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 128, 0, a.causal, a.scale);
+        hipLaunchKernelGGL((qk_kernel<128>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 128, 0, a.causal, a.scale, kQkChunk);
     else {
         // two head-dim sub-tiles, summed into S before the softmax
-        hipLaunchKernelGGL((qk_kernel<512>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 512, 0, a.causal, a.scale);
+        hipLaunchKernelGGL((qk_kernel<512>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 512, 0, a.causal, a.scale, kQkChunk);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -838,9 +849,10 @@ hipError_t launch_bwd512(const BwdArgs& a) {
     const _Float16* v = (const _Float16*)a.v;
     const _Float16* dO = (const _Float16*)a.dout;
     const int TQ = (S + 63) / 64;
+    const int kQkChunk = qk_chunk(512, BH, TQ);
     const dim3 qk_grid((unsigned)(BH * TQ * ((TQ + kQkChunk - 1) / kQkChunk)));
-    hipLaunchKernelGGL((qk_kernel<512>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 512, 0, a.causal, a.scale);
-    hipLaunchKernelGGL((qk_kernel<512>), qk_grid, dim3(256), 0, st, dO, v, dPm, BH, S, Sp, 512, 0, a.causal, 1.0f);
+    hipLaunchKernelGGL((qk_kernel<512>), qk_grid, dim3(256), 0, st, q, k, Sm, BH, S, Sp, 512, 0, a.causal, a.scale, kQkChunk);
+    hipLaunchKernelGGL((qk_kernel<512>), qk_grid, dim3(256), 0, st, dO, v, dPm, BH, S, Sp, 512, 0, a.causal, 1.0f, kQkChunk);
     const int BHS = BH * S;
     hipLaunchKernelGGL(bwd512_delta_kernel, dim3((unsigned)((BHS + 3) / 4)), dim3(256), 0, st, dO,
                        (const _Float16*)a.o, dlt, BHS);
