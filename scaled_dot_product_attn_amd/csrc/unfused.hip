@@ -387,8 +387,13 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
     // the P rows q0 .. q0 + BM - 1 of the workgroup (rows past S read zero)
     const auto prs = rsrc(P + ((size_t)bh * S + q0) * Sp, (uint32_t)min(S - q0, G::BM) * Sp * 2);
     auto swzp = [](int r) { return (r >> 1) & 7; };
-    const int kend = causal ? min(S, q0 + G::BM) : S;
+    // causal = 1: rows see keys up to their own (lower triangle); causal = 2:
+    // rows see keys from their own on (upper triangle: P^T and dS^T of a
+    // causal call, zero below the diagonal), so the walk starts at the
+    // diagonal tile
+    const int kend = causal == 1 ? min(S, q0 + G::BM) : S;
     const int nT = (kend + G::BN - 1) / G::BN;
+    const int t0 = causal == 2 ? q0 / G::BN : 0;
 
     floatx16 o[G::DW / 32];
 #pragma unroll
@@ -438,8 +443,8 @@ pv_kernel(const _Float16* __restrict__ P, const _Float16* __restrict__ V, _Float
     // the next tile's loads go out after this tile's stores to LDS,
     // unconditionally (past the last tile re-reading it) so that the wait
     // counts stay exact
-    load(0);
-    for (int t = 0; t < nT; ++t) {
+    load(t0);
+    for (int t = t0; t < nT; ++t) {
         store();
         barrier();
         load(min(t + 1, nT - 1));
@@ -860,9 +865,10 @@ hipError_t launch_bwd512(const BwdArgs& a) {
                        a.lse, dlt, dS, PT, dST, S, Sp, TQ, a.causal, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // dV = P^T dO, dK = dS^T Q (rows = keys, every column), dQ = dS K (causal rows)
-    pv512(st, PT, dO, (_Float16*)a.dv, BH, S, Sp, 0);
-    pv512(st, dST, q, (_Float16*)a.dk, BH, S, Sp, 0);
+    // dV = P^T dO, dK = dS^T Q (rows = keys; causal: the queries from the key
+    // on), dQ = dS K (causal rows)
+    pv512(st, PT, dO, (_Float16*)a.dv, BH, S, Sp, a.causal ? 2 : 0);
+    pv512(st, dST, q, (_Float16*)a.dk, BH, S, Sp, a.causal ? 2 : 0);
     pv512(st, dS, k, (_Float16*)a.dq, BH, S, Sp, (int)a.causal);
     return hipGetLastError();
 }
